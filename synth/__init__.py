@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the NVFP4 quantize / GEMM workloads.
+
+This module holds no part of the quantization method: it only draws the input tensors (shapes,
+value distributions, outlier structure and MoE routing) that both the HIP library and the CPU
+oracle are fed with.  It uses PyTorch's CPU generator only (deterministic for a given seed and
+shape, independent of any GPU).
+
+Workloads (shapes stand in for the Llama-3-8B / Llama-3.1-405B FFN and the MoE expert layers that
+the pages' throughput and checkpoint results are quoted on; no dataset or trained weight is used):
+  tiny      A, B [64 x 64] fp32 ~N(0,1), 1% of entries x50
+  fprop8b   X [8192 x 4096] bf16 ~N(0,1), 0.1% of channels (columns) x20; W [14336 x 4096] ~N(0,0.02)
+  wgrad8b   dY [8192 x 14336] bf16 ~N(0,1e-3); X [8192 x 4096] ~N(0,1)
+  moe       64 experts W_e [4096 x 1536] = 0.02 * Student-t(nu=4); X [16384 x 4096] ~N(0,1);
+            top-2 routing with Zipf(1.1) expert loads
+  fprop405b X [8192 x 16384] ~N(0,1), 0.1% channels x20; W [53248 x 16384] ~N(0,0.01)
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _gen(seed: int, tensor_id: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed((int(seed) * 1_000_003 + int(tensor_id) * 7919 + 12345) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
+
+
+def normal(shape, std=1.0, seed=0, tensor_id=0, dtype=torch.bfloat16) -> torch.Tensor:
+    """i.i.d. N(0, std^2) in fp32, rounded (RNE) to `dtype`."""
+    x = torch.randn(shape, generator=_gen(seed, tensor_id), dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+def outlier_columns(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_id=0) -> torch.Tensor:
+    """Scale round(frac * ncols) seeded columns (channels) of x by `factor` (in place, fp32 math)."""
+    ncol = x.shape[1]
+    n = int(round(frac * ncol))
+    if n == 0:
+        return x
+    cols = torch.randperm(ncol, generator=_gen(seed, tensor_id + 100))[:n]
+    x[:, cols] = (x[:, cols].float() * factor).to(x.dtype)
+    return x
+
+
+def outlier_entries(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_id=0) -> torch.Tensor:
+    """Scale round(frac * numel) seeded entries of x by `factor` (in place)."""
+    n = int(round(frac * x.numel()))
+    idx = torch.randperm(x.numel(), generator=_gen(seed, tensor_id + 200))[:n]
+    flat = x.view(-1)
+    flat[idx] = (flat[idx].float() * factor).to(x.dtype)
+    return x
+
+
+def student_t(shape, nu=4, scale=1.0, seed=0, tensor_id=0, dtype=torch.bfloat16) -> torch.Tensor:
+    """scale * t_nu with t = z0 / sqrt(sum_{i=1..nu} z_i^2 / nu), z ~ N(0,1); computed in fp64."""
+    g = _gen(seed, tensor_id)
+    z0 = torch.randn(shape, generator=g, dtype=torch.float64)
+    chi = torch.zeros(shape, dtype=torch.float64)
+    for _ in range(nu):
+        z = torch.randn(shape, generator=g, dtype=torch.float64)
+        chi.add_(z * z)
+    t = z0 / torch.sqrt(chi / nu)
+    return (t * scale).to(dtype)
+
+
+def zipf_loads(n_experts=64, total=32768, s=1.1, seed=0) -> np.ndarray:
+    """Per-expert row counts: Zipf(s) probabilities over expert ranks, ranks mapped to experts by a
+    seeded permutation, counts by largest-remainder rounding of total * p (sum == total)."""
+    ranks = np.arange(1, n_experts + 1, dtype=np.float64)
+    p = ranks ** (-s)
+    p /= p.sum()
+    raw = total * p
+    m = np.floor(raw).astype(np.int64)
+    rem = total - int(m.sum())
+    order = np.argsort(-(raw - m), kind="stable")
+    m[order[:rem]] += 1
+    perm = torch.randperm(n_experts, generator=_gen(seed, 900)).numpy()
+    loads = np.zeros(n_experts, dtype=np.int64)
+    loads[perm] = m  # rank r -> expert perm[r]
+    return loads
+
+
+def moe_routing(n_tokens=16384, n_experts=64, topk=2, s=1.1, seed=0):
+    """Top-2 routing with Zipf loads.  Returns (loads[E], slot_token[n_tokens*topk]) where the slots
+    are expert-sorted: rows offsets[e]:offsets[e+1] of the grouped activation matrix belong to
+    expert e and slot_token[j] is the token feeding row j.  Token t takes slots t and t + n_tokens
+    of the expert-sorted slot list (always two distinct experts when every load < n_tokens), then
+    tokens are relabelled by a seeded permutation."""
+    total = n_tokens * topk
+    loads = zipf_loads(n_experts, total, s, seed)
+    assert loads.max() < n_tokens
+    slot_token = np.empty(total, dtype=np.int64)
+    base = np.arange(n_tokens, dtype=np.int64)
+    for k in range(topk):
+        slot_token[k * n_tokens:(k + 1) * n_tokens] = base
+    relabel = torch.randperm(n_tokens, generator=_gen(seed, 901)).numpy()
+    slot_token = relabel[slot_token]
+    return loads, slot_token
+
+
+# ---- the workloads ---------------------------------------------------------------------------
+
+def tiny(seed=0):
+    a = normal((64, 64), 1.0, seed, 1, torch.float32)
+    b = normal((64, 64), 1.0, seed, 2, torch.float32)
+    outlier_entries(a, 0.01, 50.0, seed, 1)
+    outlier_entries(b, 0.01, 50.0, seed, 2)
+    return a, b
+
+
+def fprop8b(seed=0, m=8192, n=14336, k=4096):
+    x = normal((m, k), 1.0, seed, 3)
+    outlier_columns(x, 0.001, 20.0, seed, 3)
+    w = normal((n, k), 0.02, seed, 4)
+    return x, w
+
+
+def wgrad8b(seed=0, tokens=8192, n_out=14336, n_in=4096):
+    dy = normal((tokens, n_out), 1e-3, seed, 5)
+    x = normal((tokens, n_in), 1.0, seed, 6)
+    return dy, x
+
+
+def moe_experts(seed=0, n_experts=64, k=4096, n=1536):
+    return [student_t((k, n), 4, 0.02, seed, 1000 + e) for e in range(n_experts)]
+
+
+def moe_tokens(seed=0, n_tokens=16384, k=4096):
+    return normal((n_tokens, k), 1.0, seed, 7)
+
+
+def fprop405b(seed=0, m=8192, n=53248, k=16384):
+    x = normal((m, k), 1.0, seed, 8)
+    outlier_columns(x, 0.001, 20.0, seed, 8)
+    w = normal((n, k), 0.01, seed, 9)
+    return x, w
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw uint16 bit patterns of a bf16 CPU tensor (what the oracle takes for bf16 inputs)."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
