@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 quantize-and-multiply path on one MI355X.
+
+Default workload (the Llama-3-8B FFN forward shape): X [8192 x 4096] bf16 ~N(0,1) with 0.1% outlier
+channels x20, W [14336 x 4096] bf16 ~N(0,0.02).  One step = nvfp4_quantize(X) (1D blocks) +
+nvfp4_quantize(W) (16x16 tiles) + nvfp4_gemm(X_q, W_q) -> Y [8192 x 14336] bf16, FP32 accumulate.
+Inputs are generated once and resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step
+time); the components object carries the quantize GB/s (algorithmic bytes: both passes' reads plus
+the codes and scales written) and the GEMM-only TFLOP/s; `roofline` describes the dominant kernel
+(the GEMM) against the MI355X dense fp16 MFMA peak; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload fprop8b|wgrad8b] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+METRIC = "NVFP4 quantize HBM GB/s + NVFP4 GEMM TFLOP/s (8192x14336x4096)"
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b"])
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=512, help="rows of X and W in the CPU sample")
+    return p.parse_args()
+
+
+def quant_bytes(rows, cols, block2d):
+    """Algorithmic HBM bytes of one quantize of a bf16 tensor: two reads (amax pass, encode pass),
+    the packed codes and the scale bytes."""
+    n = rows * cols
+    return n * 2 + n * 2 + n // 2 + (n // 256 if block2d else n // 16)
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import nvfp4_bit_block_quantize_amd as nv
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    nv.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if a.workload == "fprop8b":
+        x_cpu, w_cpu = synth.fprop8b(0)
+        M, K = x_cpu.shape
+        N = w_cpu.shape[0]
+        fa, fb, rht = 0, nv.NVFP4_BLOCK2D, False
+        out_dtype = torch.bfloat16
+        workload = "Llama-3-8B FFN fprop: X[8192x4096] bf16 1D blocks, W[14336x4096] bf16 16x16 tiles, Y bf16"
+        qbytes = quant_bytes(M, K, False) + quant_bytes(N, K, True)
+    else:
+        dy_cpu, xx_cpu = synth.wgrad8b(0)
+        x_cpu, w_cpu = dy_cpu, xx_cpu  # A = dY^T, B = X^T
+        K, M = x_cpu.shape
+        N = w_cpu.shape[1]
+        fa, fb, rht = nv.NVFP4_COLWISE | nv.NVFP4_SR, nv.NVFP4_COLWISE, True
+        out_dtype = torch.float32
+        workload = "Llama-3-8B FFN wgrad: RHT(dY)[8192x14336] SR, RHT(X)[8192x4096], dW fp32"
+        qbytes = quant_bytes(K, M, False) + quant_bytes(K, N, False)
+    x = x_cpu.to(dev)
+    w = w_cpu.to(dev)
+    del x_cpu, w_cpu
+    R_a, K_a = (x.shape[1], x.shape[0]) if fa & nv.NVFP4_COLWISE else tuple(x.shape)
+    R_b, K_b = (w.shape[1], w.shape[0]) if fb & nv.NVFP4_COLWISE else tuple(w.shape)
+    qa = nv.empty_like_quantized(R_a, K_a, fa, dev)
+    qb = nv.empty_like_quantized(R_b, K_b, fb, dev)
+    ws_a = torch.empty(nv.nvfp4_workspace_size(*x.shape, fa) // 4, dtype=torch.int32, device=dev)
+    ws_b = torch.empty(nv.nvfp4_workspace_size(*w.shape, fb) // 4, dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=out_dtype, device=dev)
+
+    def q_a():
+        if rht:
+            nv.nvfp4_rht_quantize(x, 7, flags=fa, seed=7, out=qa, workspace=ws_a)
+        else:
+            nv.nvfp4_quantize(x, flags=fa, out=qa, workspace=ws_a)
+
+    def q_b():
+        if rht:
+            nv.nvfp4_rht_quantize(w, 7, flags=fb, out=qb, workspace=ws_b)
+        else:
+            nv.nvfp4_quantize(w, flags=fb, out=qb, workspace=ws_b)
+
+    def mm():
+        nv.nvfp4_gemm(qa, qb, out=y)
+
+    for _ in range(a.warmup):
+        q_a(); q_b(); mm()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        e = evs[s]
+        e[0].record(); q_a(); e[1].record(); q_b(); e[2].record(); mm(); e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    qa_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
+    qb_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
+    mm_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
+    ms_step = wall * 1e3 / a.steps
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (mm_ms * 1e-3) / 1e12
+    quant_gbps = qbytes / ((qa_ms + qb_ms) * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 x e4m3) -> exact f16 operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": workload, "M": M, "N": N, "K": K, "out": str(out_dtype).replace("torch.", "")},
+        "components": {
+            "quantize_gbps": round(quant_gbps, 1),
+            "quantize_hbm_frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
+            "quantize_a_ms": round(qa_ms, 4),
+            "quantize_b_ms": round(qb_ms, 4),
+            "quantize_algorithmic_bytes": qbytes,
+            "gemm_ms": round(mm_ms, 4),
+            "gemm_tflops": round(gemm_tflops, 1),
+        },
+        "roofline": {
+            "kernel": "nvfp4 gemm",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not a.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(a, nv)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(a, nv):
+    """The CPU oracle (as it stands) on a bounded sample of the step: quantize the first rows of X
+    and of W, then the binary64 GEMM of the two samples over the full K.  Reported in the step's
+    unit (TFLOP/s of 2*m*n*K)."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = a.cpu_rows
+    x_cpu, w_cpu = synth.fprop8b(0)
+    xs = synth.bf16_bits(x_cpu[:rows].contiguous())
+    wsmp = synth.bf16_bits(w_cpu[:rows].contiguous())
+    K = xs.shape[1]
+    t0 = time.perf_counter()
+    qx = oracle.quantize(xs, nthreads=threads)
+    qw = oracle.quantize(wsmp, flags=oracle.BLOCK2D, nthreads=threads)
+    t1 = time.perf_counter()
+    oracle.gemm_ref(qx, qw, rows, rows, K, nthreads=threads)
+    t2 = time.perf_counter()
+    flops = 2.0 * rows * rows * K
+    qbytes = quant_bytes(rows, K, False) + quant_bytes(rows, K, True)
+    return {
+        "value": round(flops / (t2 - t0) / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"quantize X[:{rows}] (1D) and W[:{rows}] (2D), binary64 GEMM {rows}x{rows}x{K}",
+        "seconds": round(t2 - t0, 3),
+        "quantize_gbps": round(qbytes / (t1 - t0) / 1e9, 3),
+        "gemm_gflops": round(flops / (t2 - t1) / 1e9, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+// nvfp4_api.cpp -- C ABI front end of libnvfp4.so: argument validation on the host, then the
+// kernel launchers.  Validation never touches the GPU, so every error path can be exercised on a
+// machine without one.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "nvfp4_internal.h"
+
+namespace {
+
+constexpr uint32_t kKnownFlags = NVFP4_COLWISE | NVFP4_BLOCK2D | NVFP4_SR | NVFP4_FOUR_OVER_SIX;
+constexpr int64_t kMaxIndex = int64_t(1) << 32;  // element / chunk counts are 32-bit in the kernels
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dtype_size(int dt) { return dt == NVFP4_F32 ? 4 : (dt == NVFP4_BF16 ? 2 : 0); }
+
+int check_flags(uint32_t flags, bool rht) {
+  if (flags & ~kKnownFlags) return NVFP4_ERR_UNSUPPORTED;
+  const bool sr = flags & NVFP4_SR, fos = flags & NVFP4_FOUR_OVER_SIX, b2d = flags & NVFP4_BLOCK2D;
+  if ((sr && fos) || (sr && b2d) || (fos && b2d) || (rht && b2d)) return NVFP4_ERR_UNSUPPORTED;
+  return NVFP4_OK;
+}
+
+// Shared validation of the quantize entry points; fills R, K.
+int validate_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
+                      bool rht, const nvfp4_tensor *out, const void *workspace, int64_t *R, int64_t *K) {
+  if (!out) return NVFP4_ERR_NULL;
+  const int es = dtype_size(x_dtype);
+  if (es == 0) return NVFP4_ERR_UNSUPPORTED;
+  int st = check_flags(flags, rht);
+  if (st != NVFP4_OK) return st;
+  if (rows < 0 || cols < 0 || ldx < cols || ldx < 1) return NVFP4_ERR_SHAPE;
+  const bool colwise = flags & NVFP4_COLWISE;
+  *R = colwise ? cols : rows;
+  *K = colwise ? rows : cols;
+  if (*K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((flags & NVFP4_BLOCK2D) && *R % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (colwise && cols % 8 != 0) return NVFP4_ERR_SHAPE;  // a lane reads 8 columns
+  if (rows * cols >= kMaxIndex || rows * ldx >= kMaxIndex * 4) return NVFP4_ERR_SHAPE;
+  if (out->rows != *R || out->k != *K || ((out->flags ^ flags) & NVFP4_BLOCK2D)) return NVFP4_ERR_SHAPE;
+  if (*R == 0 || *K == 0) {
+    if (!out->tensor_scale) return NVFP4_ERR_NULL;
+    return NVFP4_OK;
+  }
+  if (!x || !out->data || !out->scales || !out->tensor_scale || !workspace) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out->data) || !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+  if ((ldx * es) % 16 != 0) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+int run_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
+                 uint64_t seed, uint32_t stream_id, bool rht, uint64_t sign_seed, float *rht_out,
+                 nvfp4_tensor *out, void *workspace, void *hip_stream) {
+  int64_t R = 0, K = 0;
+  int st = validate_quantize(x, x_dtype, rows, cols, ldx, flags, rht, out, workspace, &R, &K);
+  if (st != NVFP4_OK) return st;
+  if (rht_out && !aligned16(rht_out)) return NVFP4_ERR_ALIGN;
+  nvfp4::QuantArgs a{};
+  a.x = x;
+  a.dtype = x_dtype == NVFP4_BF16 ? 1 : 0;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.R = R;
+  a.K = K;
+  a.flags = flags;
+  a.seed = seed;
+  a.stream_id = stream_id;
+  a.rht = rht;
+  a.sign_word = 0;
+  if (rht) {
+    const uint32_t ctr[4] = {0u, 0u, 0u, 1u};
+    const uint32_t key[2] = {static_cast<uint32_t>(sign_seed), static_cast<uint32_t>(sign_seed >> 32)};
+    uint32_t w[4];
+    nvfp4::philox4x32_10_host(ctr, key, w);
+    a.sign_word = w[0] & 0xFFFFu;
+  }
+  a.rht_out = rht ? rht_out : nullptr;
+  a.data = out->data;
+  a.scales = out->scales;
+  a.ts = out->tensor_scale;
+  a.workspace = static_cast<uint32_t *>(workspace);
+  a.stream = static_cast<hipStream_t>(hip_stream);
+  return status_of(nvfp4::launch_quantize(a));
+}
+
+}  // namespace
+
+namespace nvfp4 {
+void philox4x32_10_host(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c1 = static_cast<uint32_t>(p1);
+    c3 = static_cast<uint32_t>(p0);
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+}  // namespace nvfp4
+
+extern "C" {
+
+size_t nvfp4_workspace_size(int64_t rows, int64_t cols, uint32_t flags) {
+  (void)rows;
+  (void)cols;
+  (void)flags;
+  return sizeof(uint32_t) * nvfp4::kMaxParts;
+}
+
+int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
+                   uint64_t seed, uint32_t stream_id, nvfp4_tensor *out, void *workspace, void *hip_stream) {
+  return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, false, 0, nullptr, out, workspace,
+                      hip_stream);
+}
+
+int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
+                       uint64_t seed, uint32_t stream_id, uint64_t sign_seed, float *rht_out, nvfp4_tensor *out,
+                       void *workspace, void *hip_stream) {
+  return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, true, sign_seed, rht_out, out, workspace,
+                      hip_stream);
+}
+
+int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int y_dtype, int64_t ldy, void *hip_stream) {
+  if (!in) return NVFP4_ERR_NULL;
+  const int es = dtype_size(y_dtype);
+  if (es == 0) return NVFP4_ERR_UNSUPPORTED;
+  if (in->rows < 0 || in->k < 0 || in->k % 16 != 0 || ldy < in->k || ldy < 1) return NVFP4_ERR_SHAPE;
+  if ((in->flags & NVFP4_BLOCK2D) && in->rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (in->rows * in->k >= kMaxIndex) return NVFP4_ERR_SHAPE;
+  if (in->rows == 0 || in->k == 0) return NVFP4_OK;
+  if (!in->data || !in->scales || !in->tensor_scale || !y) return NVFP4_ERR_NULL;
+  if (!aligned16(in->data) || !aligned16(y) || (ldy * es) % 16 != 0) return NVFP4_ERR_ALIGN;
+  nvfp4::DequantArgs a{in->data, in->scales, in->tensor_scale, in->rows, in->k,
+                       (in->flags & NVFP4_BLOCK2D) != 0, y, y_dtype == NVFP4_BF16 ? 1 : 0, ldy,
+                       static_cast<hipStream_t>(hip_stream)};
+  return status_of(nvfp4::launch_dequantize(a));
+}
+
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, int32_t num_groups,
+               const int64_t *group_row_offsets, void *hip_stream) {
+  if (!a || !b) return NVFP4_ERR_NULL;
+  if (dtype_size(c_dtype) == 0) return NVFP4_ERR_UNSUPPORTED;
+  if (num_groups < 0 || (num_groups > 1 && !group_row_offsets)) return NVFP4_ERR_SHAPE;
+  const int64_t M = a->rows, N = b->rows, K = a->k;
+  if (M < 0 || N < 0 || K < 0 || b->k != K || K % 16 != 0 || ldc < N || ldc < 1) return NVFP4_ERR_SHAPE;
+  if ((a->flags & NVFP4_BLOCK2D) && M % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((b->flags & NVFP4_BLOCK2D) && N % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M * K >= kMaxIndex || N * K >= kMaxIndex || M * ldc >= kMaxIndex * 4) return NVFP4_ERR_SHAPE;
+  if (num_groups > 1 || group_row_offsets) {
+    const int32_t G = num_groups < 1 ? 1 : num_groups;
+    if (group_row_offsets[0] != 0 || group_row_offsets[G] != M) return NVFP4_ERR_SHAPE;
+    for (int32_t g = 0; g < G; ++g)
+      if (group_row_offsets[g + 1] < group_row_offsets[g]) return NVFP4_ERR_SHAPE;
+  }
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a->data || !a->scales || !a->tensor_scale || !b->data || !b->scales || !b->tensor_scale || !c)
+    return NVFP4_ERR_NULL;
+  if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(c) & static_cast<uintptr_t>(dtype_size(c_dtype) - 1)) != 0) return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g{};
+  g.a_data = a->data;
+  g.a_scales = a->scales;
+  g.a_ts = a->tensor_scale;
+  g.a_2d = (a->flags & NVFP4_BLOCK2D) != 0;
+  g.b_data = b->data;
+  g.b_scales = b->scales;
+  g.b_ts = b->tensor_scale;
+  g.b_2d = (b->flags & NVFP4_BLOCK2D) != 0;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c = c;
+  g.c_dtype = c_dtype == NVFP4_BF16 ? 1 : 0;
+  g.ldc = ldc;
+  g.num_groups = num_groups < 1 ? 1 : num_groups;
+  g.group_offsets = group_row_offsets;
+  g.stream = static_cast<hipStream_t>(hip_stream);
+  return status_of(nvfp4::launch_gemm(g));
+}
+
+const char *nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK: success";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: invalid shape, leading dimension or descriptor";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: pointer or leading dimension not 16-byte aligned";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED: unsupported dtype or flag combination";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: a HIP launch failed";
+    default: return "unknown nvfp4 status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+// nvfp4_device.hpp -- device-side building blocks of the NVFP4 kernels (gfx950).
+//
+// Every floating-point step that decides a bit of the output is one IEEE binary32 operation, in
+// the order the library's format definition lists (include/nvfp4.h).  The sources are compiled
+// with -ffp-contract=off so that no multiply and add are fused unless written as fmaf, and '/' is
+// the correctly rounded division sequence (v_div_scale / v_div_fmas / v_div_fixup).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+enum Mode : int { kRNE = 0, kSR = 1, kFourOverSix = 2 };
+
+// ---- bf16 / f32 unpacking --------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---- E4M3 (FN) block scale -------------------------------------------------------------------
+// Round s in [0, 448] to the nearest E4M3FN value, ties to even mantissa.  Returns the byte and
+// the decoded value (the rounded fp32 number itself).
+__device__ __forceinline__ uint32_t e4m3_rne(float s, float &S) {
+  if (s < 0.015625f) {                         // below 2^-6: E4M3 subnormals, spacing 2^-9
+    float m = __builtin_rintf(s * 512.0f);     // exact scaling, then nearest-even integer 0..8
+    S = m * 0.001953125f;
+    return static_cast<uint32_t>(m);           // m == 8 encodes 2^-6, the smallest normal
+  }
+  uint32_t b = __float_as_uint(s);
+  uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;  // keep 3 mantissa bits, RNE
+  S = __uint_as_float(r);
+  return (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // exponent rebias 127 -> 7
+}
+
+// Block scale for block maximum ab and grid target T (6, or 4 under Four-over-Six).
+__device__ __forceinline__ uint32_t block_scale(float ab, float T, float ts, float &S) {
+  if (ts == 0.0f) {
+    S = 0.0f;
+    return 0u;
+  }
+  float q = ab / T;
+  float s = q / ts;
+  s = fminf(s, 448.0f);
+  return e4m3_rne(s, S);
+}
+
+// Per-block encode factor e = RN(1 / RN(S * ts)); 0 for a zero scale (every code is then a signed
+// zero).  e is +inf only when S * ts underflows, a degenerate case handled element-wise.
+__device__ __forceinline__ float encode_factor(float S, float ts) {
+  if (S == 0.0f) return 0.0f;
+  float d = S * ts;
+  return 1.0f / d;
+}
+
+// ---- E2M1 element rounding ---------------------------------------------------------------------
+// v >= 0 (not NaN): index 0..7 of the nearest value of {0,0.5,1,1.5,2,3,4,6}, ties to the even
+// index, saturating at 6.  Below 1 the grid has spacing 0.5: adding 2^22 (whose ulp is 0.5) rounds
+// to it nearest-even.  From 1 up the grid is the floats with one mantissa bit: round the fp32
+// mantissa to one bit (nearest-even) and read exponent and bit as the index.
+__device__ __forceinline__ uint32_t e2m1_rne_index(float v) {
+  float vc = fminf(v, 6.0f);
+  uint32_t small = __float_as_uint(vc + 4194304.0f) & 7u;
+  uint32_t b = __float_as_uint(vc);
+  uint32_t big = ((b + 0x11FFFFFu + ((b >> 22) & 1u)) >> 22) & 15u;
+  return vc < 1.0f ? small : big;
+}
+
+// Stochastic rounding of v >= 0 with 16 random bits r16: between the grid neighbours lo <= v < hi
+// round up iff r16 < f * 65536, f = (v - lo) / (hi - lo) (exact); v >= 6 gives 6.
+__device__ __forceinline__ uint32_t e2m1_sr_index(float v, uint32_t r16) {
+  if (v >= 6.0f) return 7u;
+  uint32_t idx;
+  float f16;  // f * 65536, exact
+  if (v < 1.0f) {
+    bool half = v >= 0.5f;
+    float lo = half ? 0.5f : 0.0f;
+    idx = half ? 1u : 0u;
+    f16 = (v - lo) * 131072.0f;  // step 0.5
+  } else {
+    uint32_t b = __float_as_uint(v);
+    float lo = __uint_as_float(b & 0xFFC00000u);  // truncate to one mantissa bit
+    idx = (b >> 22) - 252u;                         // 1 -> 2, 1.5 -> 3, 2 -> 4, ..., 4 -> 6
+    // step = 2^(e-1) for v in [2^e, 2^(e+1)); 65536 / step = 2^(17 - e)
+    float scale = __uint_as_float((271u - (b >> 23)) << 23);
+    f16 = (v - lo) * scale;
+  }
+  return idx + ((static_cast<float>(r16) < f16) ? 1u : 0u);
+}
+
+// ---- Philox4x32-10 -------------------------------------------------------------------------------
+// Counter-based generator of Salmon et al. (SC 2011): ten rounds of two 32x32->64 multiplies with
+// the multipliers 0xD2511F53 / 0xCD9E8D57, key bumped by the Weyl increments 0x9E3779B9 /
+// 0xBB67AE85 between rounds.
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    uint32_t p0_hi = __umulhi(0xD2511F53u, c0), p0_lo = 0xD2511F53u * c0;
+    uint32_t p1_hi = __umulhi(0xCD9E8D57u, c2), p1_lo = 0xCD9E8D57u * c2;
+    uint32_t n0 = p1_hi ^ c1 ^ k0;
+    uint32_t n2 = p0_hi ^ c3 ^ k1;
+    c0 = n0;
+    c1 = p1_lo;
+    c2 = n2;
+    c3 = p0_lo;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// The 16 random bits of element i (logical index r*K + k) live in the Philox block for i >> 3.
+__device__ __forceinline__ uint32_t r16_of(const u32x4 &w, uint32_t j /* i & 7 */) {
+  uint32_t word = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
+  return (word >> (16u * (j & 1u))) & 0xFFFFu;
+}
+
+// ---- 16-point random Hadamard transform (in registers) -------------------------------------------
+// u <- (1/4) H16 D u: signs from the low 16 bits of sign_word, then the radix-2 butterfly with
+// strides 1, 2, 4, 8 (a + b to the lower, a - b to the upper slot), then the exact multiply by 1/4.
+__device__ __forceinline__ void rht16(float (&u)[16], uint32_t sign_word) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) u[t] = __uint_as_float(__float_as_uint(u[t]) ^ (((sign_word >> t) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * h) {
+#pragma unroll
+      for (int m = i; m < i + h; ++m) {
+        float a = u[m], b = u[m + h];
+        u[m] = a + b;
+        u[m + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) u[t] = u[t] * 0.25f;
+}
+
+// ---- fast division by a run-time invariant 32-bit divisor ----------------------------------------
+// Granlund & Montgomery, "Division by invariant integers using multiplication" (PLDI 1994),
+// the unsigned round-up method: q = (t + ((n - t) >> s1)) >> s2 with t = mulhi(m, n).
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0, 0, 0};
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 0 ? l - 1 : 0;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  uint32_t t = __umulhi(f.m, n);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+// ---- wave / workgroup reductions ------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
+// Largest |x| of the whole tensor from the pass-1 partial maxima (float bits of non-negative
+// values compare like unsigned integers).  Called by every wave; no barrier.
+__device__ __forceinline__ float tensor_amax(const uint32_t *__restrict__ partial, uint32_t nparts) {
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x & 63u; i < nparts; i += 64u) m = max(m, partial[i]);
+  return __uint_as_float(wave_max_u32(m));
+}
+
+}  // namespace nvfp4

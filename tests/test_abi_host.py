@@ -1,0 +1,119 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every function that
+include/nvfp4.h declares, and rejects bad arguments on the host with the documented status codes
+before anything is enqueued (fake device addresses are never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import nvfp4_bit_block_quantize_amd as nv
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+FAKE = 0x10000  # 16-byte aligned fake device address
+MIS = 0x10008   # misaligned
+
+
+def declared():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) >= {"nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize", "nvfp4_gemm",
+                          "nvfp4_workspace_size", "nvfp4_status_string"}
+    L = nv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_\w+)", out))
+    assert set(names) <= exported
+
+
+def _desc(rows, k, flags=0, data=FAKE, scales=FAKE, ts=FAKE):
+    return nv._Tensor(data, scales, ts, rows, k, flags)
+
+
+def _q(x=FAKE, dtype=nv.NVFP4_BF16, rows=32, cols=64, ldx=64, flags=0, out=None, ws=FAKE, rht=False):
+    L = nv.lib()
+    if out is None:
+        R, K = (cols, rows) if flags & nv.NVFP4_COLWISE else (rows, cols)
+        out = _desc(R, K, flags)
+    ref = ctypes.byref(out) if out is not False else None
+    if rht:
+        return L.nvfp4_rht_quantize(x, dtype, rows, cols, ldx, flags, 0, 0, 7, None, ref, ws, None)
+    return L.nvfp4_quantize(x, dtype, rows, cols, ldx, flags, 0, 0, ref, ws, None)
+
+
+@pytest.mark.parametrize("rht", [False, True])
+def test_quantize_validation(rht):
+    assert _q(out=False, rht=rht) == nv.NVFP4_ERR_NULL
+    assert _q(x=None, rht=rht) == nv.NVFP4_ERR_NULL
+    assert _q(ws=None, rht=rht) == nv.NVFP4_ERR_NULL
+    assert _q(dtype=7, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(cols=40, ldx=40, rht=rht) == nv.NVFP4_ERR_SHAPE            # K % 16
+    assert _q(ldx=32, rht=rht) == nv.NVFP4_ERR_SHAPE                     # ldx < cols
+    assert _q(rows=-1, rht=rht) == nv.NVFP4_ERR_SHAPE
+    assert _q(flags=nv.NVFP4_COLWISE, rows=40, rht=rht) == nv.NVFP4_ERR_SHAPE  # K = rows % 16
+    assert _q(flags=nv.NVFP4_COLWISE, rows=32, cols=36, ldx=40, rht=rht) == nv.NVFP4_ERR_SHAPE  # cols % 8
+    assert _q(x=MIS, rht=rht) == nv.NVFP4_ERR_ALIGN
+    assert _q(ws=MIS, rht=rht) == nv.NVFP4_ERR_ALIGN
+    assert _q(ldx=68, rht=rht) == nv.NVFP4_ERR_ALIGN                     # 136 B rows
+    assert _q(out=_desc(32, 64, data=MIS), rht=rht) == nv.NVFP4_ERR_ALIGN
+    assert _q(out=_desc(31, 64), rht=rht) == nv.NVFP4_ERR_SHAPE          # descriptor mismatch
+    assert _q(out=_desc(32, 64, nv.NVFP4_BLOCK2D), rht=rht) == nv.NVFP4_ERR_SHAPE
+    assert _q(flags=1 << 7, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_SR | nv.NVFP4_FOUR_OVER_SIX, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_SR | nv.NVFP4_BLOCK2D, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_FOUR_OVER_SIX | nv.NVFP4_BLOCK2D, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+
+
+def test_rht_rejects_2d_and_block2d_rows():
+    assert _q(flags=nv.NVFP4_BLOCK2D, rht=True) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_BLOCK2D, rows=40, ldx=64) == nv.NVFP4_ERR_SHAPE  # R % 16 for 2D
+
+
+def test_dequantize_validation():
+    L = nv.lib()
+    assert L.nvfp4_dequantize(None, FAKE, 0, 64, None) == nv.NVFP4_ERR_NULL
+    d = _desc(32, 64)
+    assert L.nvfp4_dequantize(ctypes.byref(d), FAKE, 3, 64, None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert L.nvfp4_dequantize(ctypes.byref(d), FAKE, 0, 32, None) == nv.NVFP4_ERR_SHAPE
+    assert L.nvfp4_dequantize(ctypes.byref(_desc(32, 40)), FAKE, 0, 64, None) == nv.NVFP4_ERR_SHAPE
+    assert L.nvfp4_dequantize(ctypes.byref(_desc(40, 64, nv.NVFP4_BLOCK2D)), FAKE, 0, 64, None) == nv.NVFP4_ERR_SHAPE
+    assert L.nvfp4_dequantize(ctypes.byref(d), None, 0, 64, None) == nv.NVFP4_ERR_NULL
+    assert L.nvfp4_dequantize(ctypes.byref(d), MIS, 0, 64, None) == nv.NVFP4_ERR_ALIGN
+    assert L.nvfp4_dequantize(ctypes.byref(d), FAKE, 1, 68, None) == nv.NVFP4_ERR_ALIGN
+    assert L.nvfp4_dequantize(ctypes.byref(_desc(0, 64)), FAKE, 0, 64, None) == nv.NVFP4_OK  # empty: no-op
+
+
+def test_gemm_validation():
+    L = nv.lib()
+    a, b = _desc(64, 128), _desc(32, 128)
+    g = lambda a_, b_, c=FAKE, dt=1, ldc=32, G=1, offs=None: L.nvfp4_gemm(
+        ctypes.byref(a_) if a_ else None, ctypes.byref(b_) if b_ else None, c, dt, ldc, G, offs, None)
+    assert g(None, b) == nv.NVFP4_ERR_NULL
+    assert g(a, b, dt=5) == nv.NVFP4_ERR_UNSUPPORTED
+    assert g(a, _desc(32, 144)) == nv.NVFP4_ERR_SHAPE          # K mismatch
+    assert g(_desc(64, 120), _desc(32, 120)) == nv.NVFP4_ERR_SHAPE  # K % 16
+    assert g(a, b, ldc=16) == nv.NVFP4_ERR_SHAPE               # ldc < N
+    assert g(a, _desc(40, 128, nv.NVFP4_BLOCK2D)) == nv.NVFP4_ERR_SHAPE
+    assert g(a, b, c=None) == nv.NVFP4_ERR_NULL
+    assert g(_desc(64, 128, data=MIS), b) == nv.NVFP4_ERR_ALIGN
+    assert g(a, b, c=FAKE + 1) == nv.NVFP4_ERR_ALIGN
+    assert g(a, b, G=2) == nv.NVFP4_ERR_SHAPE                  # groups without offsets
+    offs = (ctypes.c_int64 * 3)(0, 70, 64)
+    assert g(a, b, G=2, offs=offs) == nv.NVFP4_ERR_SHAPE       # decreasing
+    offs = (ctypes.c_int64 * 3)(0, 10, 60)
+    assert g(a, b, G=2, offs=offs) == nv.NVFP4_ERR_SHAPE       # does not end at M
+    assert g(_desc(0, 128), b) == nv.NVFP4_OK                  # empty: no-op
+
+
+def test_status_strings_and_workspace():
+    for s in range(6):
+        assert nv.nvfp4_status_string(s).startswith("NVFP4_")
+    assert "unknown" in nv.nvfp4_status_string(99)
+    assert nv.nvfp4_workspace_size(8192, 4096, 0) >= 4 * 1024

@@ -1,0 +1,125 @@
+"""GPU parity of nvfp4_gemm against the oracle's binary64 block-scaled GEMM.
+
+Pass condition: |C - C_ref| <= 1e-5 * sum_k |a_ik||b_jk| per output cell (plus 2^-8 |C_ref| for a
+bf16 output, whose rounding the bound leaves out).  The GEMM inputs are the library's own
+quantized operands copied back, so the check isolates the multiply (quantize parity is tested
+separately)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_util import gemm_check, seeded_tiles
+
+pytestmark = pytest.mark.gpu
+
+nv = pytest.importorskip("nvfp4_bit_block_quantize_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nv.lib()
+
+
+def _host(q):
+    return {"data": q.data.cpu().numpy(), "scales": q.scales.cpu().numpy(),
+            "ts": q.tensor_scale.cpu().numpy()[0], "flags": q.flags}
+
+
+def _gemm_case(oracle, a, b, a_flags=0, b_flags=0, out_dtype=torch.float32, tiles=None, what=""):
+    print(f"[gemm] {what} A={tuple(a.shape)} B={tuple(b.shape)} out={out_dtype}", flush=True)
+    qa = nv.nvfp4_quantize(a.cuda(), flags=a_flags)
+    qb = nv.nvfp4_quantize(b.cuda(), flags=b_flags)
+    c = nv.nvfp4_gemm(qa, qb, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    M, N, K = qa.rows, qb.rows, qa.k
+    cref, bnd = oracle.gemm_ref(_host(qa), _host(qb), M, N, K, tiles=tiles)
+    return gemm_check(c.float().cpu().numpy(), cref, bnd, out_dtype == torch.bfloat16, what)
+
+
+def test_gemm_tiny_full(oracle):
+    a, b = synth.tiny(0)
+    rel = _gemm_case(oracle, a, b, what="tiny 64x64x64")
+    print(f"max |err| / bound = {rel:.3e}")
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 136, 80), (1, 1, 16), (129, 257, 1040), (256, 256, 4096)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_ragged_shapes(oracle, M, N, K, out_dtype):
+    a = synth.normal((M, K), 1.0, seed=1, tensor_id=60, dtype=torch.bfloat16)
+    b = synth.normal((N, K), 0.02, seed=1, tensor_id=61, dtype=torch.bfloat16)
+    _gemm_case(oracle, a, b, out_dtype=out_dtype, what=f"{M}x{N}x{K}")
+
+
+def test_gemm_2d_weight_scales(oracle):
+    a = synth.normal((96, 512), 1.0, seed=2, tensor_id=62)
+    b = synth.normal((160, 512), 0.02, seed=2, tensor_id=63)
+    _gemm_case(oracle, a, b, b_flags=nv.NVFP4_BLOCK2D, out_dtype=torch.bfloat16, what="2D B")
+    _gemm_case(oracle, a, b, a_flags=nv.NVFP4_BLOCK2D, b_flags=nv.NVFP4_BLOCK2D, what="2D A and B")
+
+
+def test_gemm_one_hot_selects_weight_row(oracle):
+    # A rows with one element 2.625 (-> ts 2^-10, scale 448, code 6: exact) pick columns of B_hat
+    K = 256
+    a = torch.zeros((8, K), dtype=torch.float32)
+    picks = [0, 31, 100, 255, 17, 64, 128, 200]
+    for i, k in enumerate(picks):
+        a[i, k] = 2.625
+    b = synth.normal((48, K), 1.0, seed=3, tensor_id=64, dtype=torch.float32)
+    qa, qb = nv.nvfp4_quantize(a.cuda()), nv.nvfp4_quantize(b.cuda())
+    c = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32).cpu()
+    yb = nv.nvfp4_dequantize(qb).cpu()
+    for i, k in enumerate(picks):
+        torch.testing.assert_close(c[i], 2.625 * yb[:, k], rtol=2 ** -22, atol=0)
+
+
+def test_gemm_grouped_small(oracle):
+    sizes = [0, 37, 128, 1, 90, 300]
+    M, N, K = sum(sizes), 96, 160
+    offs = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    a = synth.normal((M, K), 1.0, seed=4, tensor_id=65)
+    ws = [synth.normal((N, K), 0.05 * (g + 1), seed=4, tensor_id=66 + g) for g in range(len(sizes))]
+    qa = nv.nvfp4_quantize(a.cuda())
+    qws = [nv.nvfp4_quantize(w.cuda()) for w in ws]
+    G = len(sizes)
+    qb = nv.NVFP4Tensor(torch.cat([q.data for q in qws]), torch.cat([q.scales for q in qws]),
+                        torch.cat([q.tensor_scale for q in qws]), N, K, 0, G)
+    c = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32, group_offsets=offs).cpu().numpy()
+    ha = _host(qa)
+    for g in range(G):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 == r0:
+            continue
+        sub = {"data": ha["data"][r0:r1], "scales": ha["scales"][r0:r1], "ts": ha["ts"], "flags": 0}
+        cref, bnd = oracle.gemm_ref(sub, _host(qws[g]), r1 - r0, N, K)
+        gemm_check(c[r0:r1], cref, bnd, False, f"group {g}")
+
+
+def test_gemm_fprop8b_sampled_tiles(oracle):
+    x, w = synth.fprop8b(0)
+    M, N = x.shape[0], w.shape[0]
+    tiles = seeded_tiles(M, N, 64, seed=0) + [(0, 0, 1, N), (M - 1, 0, 1, N)]
+    rel = _gemm_case(oracle, x, w, b_flags=nv.NVFP4_BLOCK2D, out_dtype=torch.bfloat16, tiles=tiles,
+                     what="fprop 8192x14336x4096")
+    print(f"max |err| / bound = {rel:.3e}")
+
+
+def test_gemm_wgrad8b_rht_sampled_tiles(oracle):
+    dy, x = synth.wgrad8b(0)
+    qa = nv.nvfp4_rht_quantize(dy.cuda(), 7, flags=nv.NVFP4_COLWISE | nv.NVFP4_SR, seed=7)
+    qb = nv.nvfp4_rht_quantize(x.cuda(), 7, flags=nv.NVFP4_COLWISE)
+    c = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    M, N, K = qa.rows, qb.rows, qa.k
+    tiles = seeded_tiles(M, N, 32, seed=1)
+    cref, bnd = oracle.gemm_ref(_host(qa), _host(qb), M, N, K, tiles=tiles)
+    gemm_check(c.cpu().numpy(), cref, bnd, False, "wgrad 14336x4096x8192")
+    # the transforms cancel in the product: dW stays close to the unquantized dY^T X
+    r0, c0, h, w_ = tiles[0]
+    exact = (dy[:, r0:r0 + h].double().T @ x[:, c0:c0 + w_].double()).numpy()
+    got = c.cpu().numpy()[r0:r0 + h, c0:c0 + w_]
+    rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+    print(f"relative error of NVFP4 wgrad vs bf16 inputs on one tile: {rel:.3f}")
+    assert rel < 0.35
