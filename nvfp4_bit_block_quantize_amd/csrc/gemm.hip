@@ -7,11 +7,19 @@
 // cores (v_mfma_f32_32x32x16_f16) form exact products and accumulate in fp32, and ts_a * ts_b is
 // applied once in the epilogue.  The per-16-element scales never touch the accumulators.
 //
-// Both operands are K-major ([rows][K/2] packed codes).  In one MFMA a lane supplies 8 K-values of
-// one row of A (row = lane & 31) and the same 8 K-positions of one row of B; any assignment of K
-// positions to (lane half, slot) is valid as long as A and B use the same one.  A lane loads 16 B
-// (32 codes) per row per 64-wide K step: lane half h takes codes [32h, 32h + 32) of the step, and
-// MFMA m (m = 0..3) consumes its dword m.
+// Decode: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 turns two codes into two exact fp16 values
+// (the instruction applies only the power-of-two part of its scale operand, so the E4M3 scale is
+// applied separately), then one v_pk_mul_f16 by (S, S): about one VALU op per element.
+//
+// Tiling: a 256-thread workgroup computes a 256 x 256 tile of C; its four waves each own a
+// 128 x 128 quarter (4 x 4 MFMA tiles of 32 x 32, 256 fp32 accumulators per lane).  K advances 128
+// codes (64 bytes per row) per step through a double-buffered LDS stage:
+//   codes   [256 rows][64 B] per operand, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3)
+//   scales  [256 rows][8 blocks] as fp16 pairs (S, S), converted once per workgroup while staging,
+//           16-byte half h of row r at h ^ ((r >> 2) & 1)
+// (the XOR swizzles give conflict-free ds_read_b128 for eight consecutive rows).  Within a step,
+// lane half h of a 32-row MFMA fragment takes codes [64h, 64h + 64) of the step and MFMA m = 0..7
+// consumes its dword m; A and B use the same K assignment, which is all the product needs.
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -21,6 +29,11 @@ namespace {
 
 constexpr uint32_t kThreads = 256;
 constexpr int kMaxGroupsPerLaunch = 128;
+constexpr int BM = 256, BN = 256;  // workgroup tile
+constexpr int BKB = 64;            // bytes of codes per row per K step (128 codes)
+constexpr int kCodeBytes = BM * BKB;        // one operand's codes per stage (16 KB)
+constexpr int kScaleBytes = BM * 8 * 4;     // one operand's fp16-pair scales per stage (8 KB)
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;  // A + B
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -36,6 +49,7 @@ struct GemmKArgs {
   int64_t ldc;
   int32_t groups;
   int32_t tiles_n;
+  int32_t total_tiles;
   int64_t b_group_data;    // bytes between consecutive groups' B codes
   int64_t b_group_scales;  // bytes between consecutive groups' B scales
   int32_t group_base;      // index of the first group of this launch (for b offsets)
@@ -43,128 +57,226 @@ struct GemmKArgs {
   int32_t tile_begin[kMaxGroupsPerLaunch + 1]; // first tile of each group (prefix sums)
 };
 
-// E4M3 byte -> fp16 (exact: every E4M3 value is a normal fp16).
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float f = e == 0 ? static_cast<float>(m) * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return static_cast<_Float16>(f);
+// E4M3 byte b -> the fp16 pair (S, S) (the hardware fp8 decode is exact: every E4M3 value is a
+// normal fp16 number).
+__device__ __forceinline__ uint32_t scale_pair(uint32_t b) {
+  half2v h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b * 0x101u, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
-// fp16 bits of the E2M1 value of a 4-bit code.
-__device__ __forceinline__ uint32_t e2m1_f16_bits(uint32_t code) {
-  uint32_t m = code & 7u;
-  uint32_t mag = m >= 2u ? (m + 28u) << 9 : (m == 1u ? 0x3800u : 0u);
-  return mag | ((code & 8u) << 12);
+// 8 codes (one dword, code n at bits 4n) times (S, S) -> 8 exact fp16 values.
+__device__ __forceinline__ half8 decode8(uint32_t w, uint32_t s2bits) {
+  const half2v s2 = __builtin_bit_cast(half2v, s2bits);
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// 8 codes (one dword, code n at bits 4n) times scale S -> 8 exact fp16 values.
-__device__ __forceinline__ half8 decode8(uint32_t w, _Float16 S) {
-  half8 r;
-  half2v s2 = {S, S};
+// Per-thread staging registers for one K step of one operand: 4 x 16 B of codes, 8 scale bytes.
+struct Stage {
+  uint4 code[4];
+  uint32_t sc_lo, sc_hi;
+};
+
+// Global -> registers for rows [row0, row0 + 256) of an operand with valid rows below rows_end.
+template <bool B2D>
+__device__ __forceinline__ void load_stage(Stage &st, const uint8_t *__restrict__ data,
+                                           const uint8_t *__restrict__ scales, int64_t row0, int64_t rows_end,
+                                           int64_t K, int64_t kt) {
+  const int64_t row_bytes = K / 2, KB = K / 16;
+  const int64_t kb0 = kt * BKB;  // byte offset of this step within a row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo = e2m1_f16_bits(w >> (8 * i)), hi = e2m1_f16_bits(w >> (8 * i + 4));
-    half2v q = __builtin_bit_cast(half2v, lo | (hi << 16));
-    half2v p = q * s2;
-    r[2 * i] = p[0];
-    r[2 * i + 1] = p[1];
+    const uint32_t c = threadIdx.x + kThreads * i;
+    const int64_t r = row0 + (c >> 2);
+    const int64_t off = kb0 + 16 * (c & 3);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows_end) {
+      const uint8_t *src = data + r * row_bytes + off;
+      if (off + 16 <= row_bytes) {
+        v = *reinterpret_cast<const uint4 *>(src);
+      } else if (off + 8 <= row_bytes) {
+        const uint2 h = *reinterpret_cast<const uint2 *>(src);
+        v = make_uint4(h.x, h.y, 0, 0);
+      }
+    }
+    st.code[i] = v;
   }
-  return r;
+  // scales: thread t -> row t, 8 bytes = blocks [8 kt, 8 kt + 8)
+  const int64_t r = row0 + threadIdx.x;
+  uint32_t lo = 0, hi = 0;
+  if (r < rows_end) {
+    const uint8_t *src = scales + (B2D ? (r / 16) * KB : r * KB) + 8 * kt;
+    const int64_t nb = KB - 8 * kt;  // blocks left in the row
+    if (nb >= 8 && ((reinterpret_cast<uintptr_t>(src) & 7u) == 0)) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(src);
+      lo = v.x;
+      hi = v.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = j < nb ? src[j] : 0u;
+        if (j < 4)
+          lo |= b << (8 * j);
+        else
+          hi |= b << (8 * (j - 4));
+      }
+    }
+  }
+  st.sc_lo = lo;
+  st.sc_hi = hi;
+}
+
+// Registers -> LDS stage (codes swizzled, scales converted to fp16 pairs).
+__device__ __forceinline__ void store_stage(const Stage &st, uint8_t *codes, uint8_t *scales) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = threadIdx.x + kThreads * i;
+    const uint32_t r = c >> 2, ch = c & 3;
+    *reinterpret_cast<uint4 *>(codes + r * BKB + 16 * (ch ^ ((r >> 1) & 3))) = st.code[i];
+  }
+  const uint32_t r = threadIdx.x;
+  uint4 h0, h1;  // blocks 0..3 and 4..7
+  h0.x = scale_pair(st.sc_lo & 0xFF);
+  h0.y = scale_pair((st.sc_lo >> 8) & 0xFF);
+  h0.z = scale_pair((st.sc_lo >> 16) & 0xFF);
+  h0.w = scale_pair(st.sc_lo >> 24);
+  h1.x = scale_pair(st.sc_hi & 0xFF);
+  h1.y = scale_pair((st.sc_hi >> 8) & 0xFF);
+  h1.z = scale_pair((st.sc_hi >> 16) & 0xFF);
+  h1.w = scale_pair(st.sc_hi >> 24);
+  const uint32_t sw = (r >> 2) & 1;
+  *reinterpret_cast<uint4 *>(scales + r * 32 + 16 * sw) = h0;
+  *reinterpret_cast<uint4 *>(scales + r * 32 + 16 * (1 ^ sw)) = h1;
+}
+
+// Map a workgroup id to a tile so that each of the 8 XCDs (workgroup i runs on XCD i % 8) owns a
+// contiguous range of tiles.
+__device__ __forceinline__ int32_t xcd_tile(int32_t wg, int32_t total) {
+  if (total % 8 != 0) return wg;
+  return (wg & 7) * (total >> 3) + (wg >> 3);
 }
 
 template <bool OUT_BF16, bool A2D, bool B2D>
-__global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmKArgs p) {
-  // tile -> (group, tile_m, tile_n)
-  const int32_t tile = blockIdx.x;
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+
+  // ---- tile -> (group, tile_m, tile_n) ----
+  const int32_t tile = xcd_tile(blockIdx.x, p.total_tiles);
   int32_t g = 0;
   while (g + 1 < p.groups && p.tile_begin[g + 1] <= tile) ++g;
   const int32_t local = tile - p.tile_begin[g];
-  const int32_t tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
-  const int64_t row0 = p.row_begin[g], row1 = p.row_begin[g + 1];
+  const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
+  // walk tiles in bands of 8 tile rows: neighbouring workgroups share A rows and B columns in L2
+  int32_t tm, tn;
+  {
+    const int32_t band = 8;
+    const int32_t per_band = band * p.tiles_n;
+    const int32_t bi = local / per_band, rem = local - bi * per_band;
+    const int32_t rows_in_band = min(band, tiles_m_g - bi * band);
+    tn = rem / rows_in_band;
+    tm = bi * band + (rem - tn * rows_in_band);
+  }
+  const int64_t row_end = p.row_begin[g + 1];
   const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
   const float ts = *p.a_ts * p.b_ts[p.group_base + g];
 
+  const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t KT = (p.K + 127) / 128;
+
   const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
   const uint32_t h = lane >> 5, l32 = lane & 31u;
-  const int64_t KB = p.K / 16;
-  const int64_t m_base = row0 + static_cast<int64_t>(tm) * 128 + (wave >> 1) * 64;
-  const int64_t n_base = static_cast<int64_t>(tn) * 128 + (wave & 1) * 64;
+  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;  // wave quarter within the tile
 
-  floatx16 acc[2][2];
+  floatx16 acc[4][4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[s][t][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < p.K; k0 += 64) {
-    half8 af[2][4], bf[2][4];
+  Stage sa, sb;
+  if (KT > 0) {
+    load_stage<A2D>(sa, p.a_data, p.a_scales, m0, row_end, p.K, 0);
+    load_stage<B2D>(sb, b_data, b_scales, n0, p.N, p.K, 0);
+    store_stage(sa, smem, smem + 2 * kCodeBytes);
+    store_stage(sb, smem + kCodeBytes, smem + 2 * kCodeBytes + kScaleBytes);
+  }
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) {
+      load_stage<A2D>(sa, p.a_data, p.a_scales, m0, row_end, p.K, kt + 1);
+      load_stage<B2D>(sb, b_data, b_scales, n0, p.N, p.K, kt + 1);
+    }
+    const uint8_t *stage = smem + (kt & 1) * kStageBytes;
+    const uint8_t *a_codes = stage, *b_codes = stage + kCodeBytes;
+    const uint8_t *a_sc = stage + 2 * kCodeBytes, *b_sc = stage + 2 * kCodeBytes + kScaleBytes;
+
+    // fragments: 4 A and 4 B row groups of 32; per lane 64 codes (two 16 B chunks) and 4 scales
+    uint4 ac[4][2], bc[4][2], as4[4], bs4[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t ra = m_base + 32 * s + l32;
-      const int64_t rb = n_base + 32 * s + l32;
-      const int64_t kc = k0 + 32 * h;  // first K of this lane's 32 codes
-      uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
-      uint32_t sa0 = 0, sa1 = 0, sb0 = 0, sb1 = 0;
-      if (kc < p.K) {
-        const bool full = kc + 32 <= p.K;  // K % 16 == 0: either 16 or 32 codes remain
-        if (ra < row1) {
-          const uint8_t *src = p.a_data + ra * (p.K / 2) + kc / 2;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(src);
-          const uint2 hi = full ? *reinterpret_cast<const uint2 *>(src + 8) : make_uint2(0, 0);
-          wa = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const uint8_t *sc = A2D ? p.a_scales + (ra / 16) * KB + kc / 16 : p.a_scales + ra * KB + kc / 16;
-          sa0 = sc[0];
-          sa1 = full ? sc[1] : 0u;
-        }
-        if (rb < p.N) {
-          const uint8_t *src = b_data + rb * (p.K / 2) + kc / 2;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(src);
-          const uint2 hi = full ? *reinterpret_cast<const uint2 *>(src + 8) : make_uint2(0, 0);
-          wb = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const uint8_t *sc = B2D ? b_scales + (rb / 16) * KB + kc / 16 : b_scales + rb * KB + kc / 16;
-          sb0 = sc[0];
-          sb1 = full ? sc[1] : 0u;
-        }
+    for (int f = 0; f < 4; ++f) {
+      const uint32_t ra = wm + 32 * f + l32, rb = wn + 32 * f + l32;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t ch = 2 * h + q;
+        ac[f][q] = *reinterpret_cast<const uint4 *>(a_codes + ra * BKB + 16 * (ch ^ ((ra >> 1) & 3)));
+        bc[f][q] = *reinterpret_cast<const uint4 *>(b_codes + rb * BKB + 16 * (ch ^ ((rb >> 1) & 3)));
       }
-      const _Float16 SA0 = e4m3_to_f16(sa0), SA1 = e4m3_to_f16(sa1);
-      const _Float16 SB0 = e4m3_to_f16(sb0), SB1 = e4m3_to_f16(sb1);
-      af[s][0] = decode8(wa.x, SA0);
-      af[s][1] = decode8(wa.y, SA0);
-      af[s][2] = decode8(wa.z, SA1);
-      af[s][3] = decode8(wa.w, SA1);
-      bf[s][0] = decode8(wb.x, SB0);
-      bf[s][1] = decode8(wb.y, SB0);
-      bf[s][2] = decode8(wb.z, SB1);
-      bf[s][3] = decode8(wb.w, SB1);
+      as4[f] = *reinterpret_cast<const uint4 *>(a_sc + ra * 32 + 16 * (h ^ ((ra >> 2) & 1)));
+      bs4[f] = *reinterpret_cast<const uint4 *>(b_sc + rb * 32 + 16 * (h ^ ((rb >> 2) & 1)));
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 8; ++m) {
+      half8 af[4], bf[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int f = 0; f < 4; ++f) {
+        const uint4 &wa = ac[f][m >> 2];
+        const uint4 &wb = bc[f][m >> 2];
+        const uint32_t da = (m & 3) == 0 ? wa.x : (m & 3) == 1 ? wa.y : (m & 3) == 2 ? wa.z : wa.w;
+        const uint32_t db = (m & 3) == 0 ? wb.x : (m & 3) == 1 ? wb.y : (m & 3) == 2 ? wb.z : wb.w;
+        const uint32_t sa2 = (m >> 1) == 0 ? as4[f].x : (m >> 1) == 1 ? as4[f].y : (m >> 1) == 2 ? as4[f].z : as4[f].w;
+        const uint32_t sb2 = (m >> 1) == 0 ? bs4[f].x : (m >> 1) == 1 ? bs4[f].y : (m >> 1) == 2 ? bs4[f].z : bs4[f].w;
+        af[f] = decode8(da, sa2);
+        bf[f] = decode8(db, sb2);
+      }
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s][m], bf[t][m], acc[s][t], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      uint8_t *nxt = smem + ((kt + 1) & 1) * kStageBytes;
+      store_stage(sa, nxt, nxt + 2 * kCodeBytes);
+      store_stage(sb, nxt + kCodeBytes, nxt + 2 * kCodeBytes + kScaleBytes);
+    }
+    __syncthreads();
   }
 
-  // epilogue: lane holds column j = lane & 31, rows 8 * (r >> 2) + 4 * h + (r & 3)
+  // ---- epilogue: lane holds column l32 of each 32 x 32 tile, rows 8 * (r >> 2) + 4 * h + (r & 3)
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t col = n_base + 32 * t + l32;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn + 32 * j + l32;
       if (col >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m_base + 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= row1) continue;
-        const float v = acc[s][t][r] * ts;
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= row_end) continue;
+        const float v = acc[i][j][r] * ts;
         if constexpr (OUT_BF16) {
-          uint32_t b = __float_as_uint(v);
-          uint16_t hb = static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-          reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] = hb;
+          const uint32_t b = __float_as_uint(v);
+          reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] =
+              static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
         } else {
           reinterpret_cast<float *>(p.c + row * p.ldc * 4)[col] = v;
         }
@@ -177,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmKArgs p) {
 hipError_t launch_gemm(const GemmArgs &a) {
   const int32_t G = a.num_groups < 1 ? 1 : a.num_groups;
   const int64_t KB = a.K / 16;
-  const int32_t tiles_n = static_cast<int32_t>((a.N + 127) / 128);
+  const int32_t tiles_n = static_cast<int32_t>((a.N + BN - 1) / BN);
   for (int32_t g0 = 0; g0 < G; g0 += kMaxGroupsPerLaunch) {
     const int32_t ng = (G - g0) < kMaxGroupsPerLaunch ? (G - g0) : kMaxGroupsPerLaunch;
     GemmKArgs p{};
@@ -202,14 +314,15 @@ hipError_t launch_gemm(const GemmArgs &a) {
       const int64_t r1 = a.group_offsets ? a.group_offsets[g0 + g + 1] : a.M;
       p.row_begin[g] = r0;
       p.tile_begin[g] = tiles;
-      tiles += static_cast<int32_t>(((r1 - r0) + 127) / 128) * tiles_n;
+      tiles += static_cast<int32_t>(((r1 - r0) + BM - 1) / BM) * tiles_n;
     }
     p.row_begin[ng] = a.group_offsets ? a.group_offsets[g0 + ng] : a.M;
     p.tile_begin[ng] = tiles;
+    p.total_tiles = tiles;
     if (tiles == 0) continue;  // K == 0 still launches: the K loop is empty and C = 0
     const bool bf16 = a.c_dtype == 1;
 #define NVFP4_GEMM(OB, A2, B2) \
-  hipLaunchKernelGGL((gemm_simple_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
+  hipLaunchKernelGGL((gemm_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
     if (bf16) {
       if (a.a_2d && a.b_2d) NVFP4_GEMM(true, true, true);
       else if (a.a_2d) NVFP4_GEMM(true, true, false);
