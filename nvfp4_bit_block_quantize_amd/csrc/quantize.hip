@@ -7,6 +7,15 @@
 //   pass 2  every wave reduces the partial maxima itself (no atomics, no zero-initialised memory),
 //           derives ts = amax / 2688, and encodes its blocks: block amax -> E4M3 scale -> E2M1
 //           codes (nearest-even, stochastic or Four-over-Six) -> packed nibbles.
+// Pass-2 grids are persistent (a few workgroups per CU, grid-stride over the work) so that the
+// per-wave partial reduction is paid a few times per CU, and each lane issues the loads of its
+// next block before it encodes the current one.
+//
+// Nearest-even encoding uses v_cvt_scalef32_pk_fp4_f32 with scale 1.0: two fp32 values -> two
+// E2M1 codes (sign copied, ties to even, saturating at 6) packed into a chosen byte.  On MI355X
+// this instruction agrees with the format's rounding rule on every one of the 2^32 fp32 inputs
+// except NaN (checked exhaustively), so v = y * e is fed to it directly.
+//
 // Layouts:
 //   row1d_kernel   ROW mode, 1D blocks: one lane per 16-element block (32 B of bf16 in, 8 B out).
 //   row2d_kernel   ROW mode, 16x16 tiles: a lane holds 16 rows x 8 columns; a lane pair is a tile.
@@ -22,29 +31,38 @@ namespace nvfp4 {
 namespace {
 
 constexpr uint32_t kThreads = 256;
+constexpr uint32_t kPass1Parts = 512;  // amax-pass workgroups (<= kMaxParts)
+constexpr uint32_t kPass2Grid = 2048;  // persistent pass-2 workgroups (8 per CU)
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // ---- loads ----------------------------------------------------------------------------------------
-// 16 consecutive elements starting at p (32 B for bf16, 64 B for f32), widened to fp32.
+// 16 consecutive elements (32 B bf16 / 64 B f32) kept raw.
 template <int ESZ>
-__device__ __forceinline__ void load16(const uint8_t *__restrict__ p, float (&y)[16]) {
-  if constexpr (ESZ == 2) {
-    uint4 a = *reinterpret_cast<const uint4 *>(p);
-    uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+struct Raw16 {
+  uint4 v[ESZ];
+};
+
+template <int ESZ>
+__device__ __forceinline__ Raw16<ESZ> load_raw16(const uint8_t *__restrict__ p) {
+  Raw16<ESZ> r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      y[2 * i] = bf16_lo(w[i]);
-      y[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
+  for (int i = 0; i < ESZ; ++i) r.v[i] = *reinterpret_cast<const uint4 *>(p + 16 * i);
+  return r;
+}
+
+template <int ESZ>
+__device__ __forceinline__ void unpack16(const Raw16<ESZ> &r, float (&y)[16]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 a = *reinterpret_cast<const uint4 *>(p + 16 * i);
-      y[4 * i] = __uint_as_float(a.x);
-      y[4 * i + 1] = __uint_as_float(a.y);
-      y[4 * i + 2] = __uint_as_float(a.z);
-      y[4 * i + 3] = __uint_as_float(a.w);
+  for (int i = 0; i < ESZ; ++i) {
+    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (ESZ == 2) {
+        y[8 * i + 2 * j] = bf16_lo(w[j]);
+        y[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+      } else {
+        y[4 * i + j] = __uint_as_float(w[j]);
+      }
     }
   }
 }
@@ -78,10 +96,6 @@ __device__ __forceinline__ float raw8_elem(const Raw8<ESZ> &r, int c) {
 // ---- element codes --------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t sign_code(float y) { return (__float_as_uint(y) >> 28) & 8u; }
 
-__device__ __forceinline__ uint32_t code_rne(float y, float e) {
-  return e2m1_rne_index(fabsf(y) * e) | sign_code(y);
-}
-
 __device__ __forceinline__ uint32_t code_sr(float y, float e, uint32_t r16) {
   return e2m1_sr_index(fabsf(y) * e, r16) | sign_code(y);
 }
@@ -89,6 +103,16 @@ __device__ __forceinline__ uint32_t code_sr(float y, float e, uint32_t r16) {
 // e == +inf (S * ts underflowed): nonzero elements saturate to 6, zeros stay zero.
 __device__ __forceinline__ uint32_t code_degenerate(float y) {
   return (y == 0.0f ? 0u : 7u) | sign_code(y);
+}
+
+// Nearest-even codes of 8 values times e, packed (code n at bits 4n).
+__device__ __forceinline__ uint32_t pack8_rne(const float *y, float e) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * e, y[1] * e, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * e, y[3] * e, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * e, y[5] * e, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * e, y[7] * e, 1.0f, 3);
+  return w;
 }
 
 // Decode a code under scale S: RN(RN(q * S) * ts).
@@ -100,34 +124,45 @@ __device__ __forceinline__ float decode(uint32_t code, float S, float ts) {
   return p * ts;
 }
 
-// Codes of one 16-element block under the given mode.  i0 = logical index of y[0] (a multiple of
+// Packed codes of one 16-element block under factor e.  i0 = logical index of y[0] (a multiple of
 // 16), used for the stochastic-rounding counter.
 template <int MODE>
-__device__ __forceinline__ void block_codes(const float (&y)[16], float e, uint64_t i0, uint32_t key0,
-                                            uint32_t key1, uint32_t stream_id, uint32_t (&c)[16]) {
+__device__ __forceinline__ void block_words(const float (&y)[16], float e, uint64_t i0, uint32_t key0, uint32_t key1,
+                                            uint32_t stream_id, uint32_t &w0, uint32_t &w1) {
   if (__builtin_isinf(e)) {
+    w0 = 0u;
+    w1 = 0u;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) c[t] = code_degenerate(y[t]);
+    for (int t = 0; t < 8; ++t) {
+      w0 |= code_degenerate(y[t]) << (4 * t);
+      w1 |= code_degenerate(y[8 + t]) << (4 * t);
+    }
   } else if constexpr (MODE == kSR) {
-    uint64_t call = i0 >> 3;
-    u32x4 r0 = philox4x32_10(static_cast<uint32_t>(call), static_cast<uint32_t>(call >> 32), stream_id, 0u, key0, key1);
-    u32x4 r1 = philox4x32_10(static_cast<uint32_t>(call + 1), static_cast<uint32_t>((call + 1) >> 32), stream_id, 0u,
-                             key0, key1);
+    const uint64_t call = i0 >> 3;
+    const u32x4 r0 = philox4x32_10(static_cast<uint32_t>(call), static_cast<uint32_t>(call >> 32), stream_id, 0u,
+                                   key0, key1);
+    const u32x4 r1 = philox4x32_10(static_cast<uint32_t>(call + 1), static_cast<uint32_t>((call + 1) >> 32),
+                                   stream_id, 0u, key0, key1);
+    w0 = 0u;
+    w1 = 0u;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) c[t] = code_sr(y[t], e, r16_of(r0, t));
-#pragma unroll
-    for (int t = 0; t < 8; ++t) c[8 + t] = code_sr(y[8 + t], e, r16_of(r1, t));
+    for (int t = 0; t < 8; ++t) {
+      w0 |= code_sr(y[t], e, r16_of(r0, t)) << (4 * t);
+      w1 |= code_sr(y[8 + t], e, r16_of(r1, t)) << (4 * t);
+    }
   } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) c[t] = code_rne(y[t], e);
+    w0 = pack8_rne(y, e);
+    w1 = pack8_rne(y + 8, e);
   }
 }
 
-__device__ __forceinline__ float block_sse(const float (&y)[16], const uint32_t (&c)[16], float S, float ts) {
+// fp32 squared error of a block against its decoded codes, accumulated with fma in block order.
+__device__ __forceinline__ float block_sse(const float (&y)[16], uint32_t w0, uint32_t w1, float S, float ts) {
   float acc = 0.0f;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    float diff = y[t] - decode(c[t], S, ts);
+    const uint32_t code = ((t < 8 ? w0 : w1) >> (4 * (t & 7))) & 15u;
+    const float diff = y[t] - decode(code, S, ts);
     acc = fmaf(diff, diff, acc);
   }
   return acc;
@@ -140,27 +175,20 @@ __device__ __forceinline__ void encode_block(const float (&y)[16], float ab, flo
                                              uint32_t &w1) {
   float S;
   sbyte = block_scale(ab, 6.0f, ts, S);
-  uint32_t c[16];
-  block_codes<MODE>(y, encode_factor(S, ts), i0, key0, key1, stream_id, c);
+  block_words<MODE>(y, encode_factor(S, ts), i0, key0, key1, stream_id, w0, w1);
   if constexpr (MODE == kFourOverSix) {
-    float acc6 = block_sse(y, c, S, ts);
+    // Four-over-Six: also map the block maximum to 4; keep it only if the block SSE is lower
+    const float acc6 = block_sse(y, w0, w1, S, ts);
     float S4;
-    uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
-    uint32_t c4[16];
-    block_codes<kRNE>(y, encode_factor(S4, ts), i0, key0, key1, stream_id, c4);
-    float acc4 = block_sse(y, c4, S4, ts);
+    const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
+    uint32_t v0, v1;
+    block_words<kRNE>(y, encode_factor(S4, ts), i0, key0, key1, stream_id, v0, v1);
+    const float acc4 = block_sse(y, v0, v1, S4, ts);
     if (acc4 < acc6) {
       sbyte = sb4;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) c[t] = c4[t];
+      w0 = v0;
+      w1 = v1;
     }
-  }
-  w0 = 0u;
-  w1 = 0u;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    w0 |= c[t] << (4 * t);
-    w1 |= c[8 + t] << (4 * t);
   }
 }
 
@@ -188,8 +216,8 @@ __device__ __forceinline__ void write_partial(uint32_t m, uint32_t *__restrict__
 // Every wave: tensor amax from the partials, ts = amax / 2688; block 0 publishes ts.
 __device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ partial, uint32_t nparts,
                                               float *__restrict__ ts_out) {
-  float A = tensor_amax(partial, nparts);
-  float ts = A / 2688.0f;
+  const float A = tensor_amax(partial, nparts);
+  const float ts = A / 2688.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
   return ts;
 }
@@ -207,12 +235,9 @@ struct AmaxArgs {
 template <int ESZ>
 __device__ __forceinline__ void absmax_chunk(const uint4 &v, u16x2 &m2, uint32_t &m4) {
   if constexpr (ESZ == 2) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u16x2 a = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
-      m2 = __builtin_elementwise_max(m2, a);
-    }
+    for (int i = 0; i < 4; ++i) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
   } else {
     m4 = max(m4, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
   }
@@ -220,25 +245,26 @@ __device__ __forceinline__ void absmax_chunk(const uint4 &v, u16x2 &m2, uint32_t
 
 template <int ESZ>
 __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs p) {
+  constexpr int U = 8;  // loads in flight per lane
   const uint32_t stride = gridDim.x * kThreads;
   u16x2 m2 = {0, 0};
   uint32_t m4 = 0;
   auto addr = [&](uint32_t c) -> const uint4 * {
     if (p.flat) return reinterpret_cast<const uint4 *>(p.x) + c;
-    uint32_t r = fdiv(c, p.cpr);
+    const uint32_t r = fdiv(c, p.cpr);
     return reinterpret_cast<const uint4 *>(p.x + static_cast<int64_t>(r) * p.ldx_bytes +
                                            static_cast<int64_t>(c - r * p.cpr.d) * 16);
   };
   uint32_t c = blockIdx.x * kThreads + threadIdx.x;
-  for (; c + 3 * stride < p.total_chunks; c += 4 * stride) {
-    uint4 v0 = *addr(c), v1 = *addr(c + stride), v2 = *addr(c + 2 * stride), v3 = *addr(c + 3 * stride);
-    absmax_chunk<ESZ>(v0, m2, m4);
-    absmax_chunk<ESZ>(v1, m2, m4);
-    absmax_chunk<ESZ>(v2, m2, m4);
-    absmax_chunk<ESZ>(v3, m2, m4);
+  for (; c + (U - 1) * stride < p.total_chunks; c += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *addr(c + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) absmax_chunk<ESZ>(v[u], m2, m4);
   }
   for (; c < p.total_chunks; c += stride) absmax_chunk<ESZ>(*addr(c), m2, m4);
-  uint32_t m = ESZ == 2 ? (static_cast<uint32_t>(max(m2.x, m2.y)) << 16) : m4;
+  const uint32_t m = ESZ == 2 ? (static_cast<uint32_t>(max(m2.x, m2.y)) << 16) : m4;
   write_partial(m, p.partial);
 }
 
@@ -261,32 +287,42 @@ struct RowArgs {
 
 template <int ESZ, int MODE, bool RHT, bool PASS1>
 __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  auto src = [&](uint32_t blk) {
+    const uint32_t r = fdiv(blk, p.kb);
+    return p.x + static_cast<int64_t>(r) * p.ldx_bytes + static_cast<int64_t>(blk - r * p.kb.d) * 16 * ESZ;
+  };
+  Raw16<ESZ> cur, nxt;
+  if (b < p.nblocks) cur = load_raw16<ESZ>(src(b));
   float ts = 0.0f;
   if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out);
   uint32_t mx = 0;
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < p.nblocks; b += stride) {
-    const uint32_t r = fdiv(b, p.kb);
-    const uint32_t kb = b - r * p.kb.d;
+  while (b < p.nblocks) {
+    const uint32_t bn = b + stride;
+    if (bn < p.nblocks) nxt = load_raw16<ESZ>(src(bn));
     float y[16];
-    load16<ESZ>(p.x + static_cast<int64_t>(r) * p.ldx_bytes + static_cast<int64_t>(kb) * 16 * ESZ, y);
+    unpack16<ESZ>(cur, y);
     if constexpr (RHT) rht16(y, p.sign_word);
     if constexpr (PASS1) {
       mx = max(mx, __float_as_uint(block_absmax(y)));
-      continue;
-    }
-    const uint64_t i0 = static_cast<uint64_t>(r) * static_cast<uint64_t>(p.K) + 16u * kb;
-    if constexpr (RHT) {
-      if (p.rht_out) {
-        float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
+    } else {
+      const uint32_t r = fdiv(b, p.kb);
+      const uint64_t i0 = static_cast<uint64_t>(r) * static_cast<uint64_t>(p.K) + 16u * (b - r * p.kb.d);
+      if constexpr (RHT) {
+        if (p.rht_out) {
+          float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+          for (int q = 0; q < 4; ++q) o[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+        }
       }
+      uint32_t sb, w0, w1;
+      encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+      *reinterpret_cast<uint2 *>(p.data + (i0 >> 1)) = make_uint2(w0, w1);
+      p.scales[i0 >> 4] = static_cast<uint8_t>(sb);
     }
-    uint32_t sb, w0, w1;
-    encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
-    *reinterpret_cast<uint2 *>(p.data + (i0 >> 1)) = make_uint2(w0, w1);
-    p.scales[i0 >> 4] = static_cast<uint8_t>(sb);
+    cur = nxt;
+    b = bn;
   }
   if constexpr (PASS1) write_partial(mx, p.partial_out);
 }
@@ -306,28 +342,40 @@ struct Row2dArgs {
 };
 
 template <int ESZ>
+__device__ __forceinline__ void load_patch(Raw8<ESZ> (&v)[16], const uint8_t *__restrict__ base, int64_t ld_bytes,
+                                           bool valid) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if (valid) {
+      v[t] = load8<ESZ>(base + t * ld_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < ESZ / 2; ++i) v[t].v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int ESZ>
 __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
-  const float ts = tensor_scale(p.partial, p.nparts, p.ts_out);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   const int64_t KB = p.K / 16;
-  for (uint32_t task = (blockIdx.x * kThreads + threadIdx.x) >> 6; task < p.ntasks; task += nwaves) {
-    const uint32_t band = fdiv(task, p.nseg);
-    const uint32_t seg = task - band * p.nseg.d;
-    const int64_t r0 = static_cast<int64_t>(band) * 16;
-    const int64_t c0 = static_cast<int64_t>(seg) * 512 + lane * 8;
+  uint32_t task = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  Raw8<ESZ> v[16];
+  auto start = [&](uint32_t tk, int64_t &r0, int64_t &c0) {
+    const uint32_t band = fdiv(tk, p.nseg);
+    r0 = static_cast<int64_t>(band) * 16;
+    c0 = static_cast<int64_t>(tk - band * p.nseg.d) * 512 + lane * 8;
+  };
+  int64_t r0 = 0, c0 = 0;
+  if (task < p.ntasks) {
+    start(task, r0, c0);
+    load_patch<ESZ>(v, p.x + r0 * p.ldx_bytes + c0 * ESZ, p.ldx_bytes, c0 < p.K);
+  }
+  const float ts = tensor_scale(p.partial, p.nparts, p.ts_out);
+  while (task < p.ntasks) {
     const bool valid = c0 < p.K;  // K % 16 == 0: both lanes of a tile agree
-    Raw8<ESZ> v[16];
     float ab = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      if (valid) {
-        v[t] = load8<ESZ>(p.x + (r0 + t) * p.ldx_bytes + c0 * ESZ);
-      } else {
-#pragma unroll
-        for (int i = 0; i < ESZ / 2; ++i) v[t].v[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
 #pragma unroll
     for (int t = 0; t < 16; ++t)
 #pragma unroll
@@ -336,19 +384,31 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
     float S;
     const uint32_t sb = block_scale(ab, 6.0f, ts, S);
     const float e = encode_factor(S, ts);
+    uint32_t w[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float yv[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) yv[c] = raw8_elem<ESZ>(v[t], c);
+      if (__builtin_isinf(e)) {
+        w[t] = 0u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[t] |= code_degenerate(yv[c]) << (4 * c);
+      } else {
+        w[t] = pack8_rne(yv, e);
+      }
+    }
+    const int64_t wr0 = r0, wc0 = c0;
+    // next task's loads go out before this task's stores
+    task += nwaves;
+    if (task < p.ntasks) {
+      start(task, r0, c0);
+      load_patch<ESZ>(v, p.x + r0 * p.ldx_bytes + c0 * ESZ, p.ldx_bytes, c0 < p.K);
+    }
     if (valid) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float yv = raw8_elem<ESZ>(v[t], c);
-          uint32_t code = __builtin_isinf(e) ? code_degenerate(yv) : code_rne(yv, e);
-          w |= code << (4 * c);
-        }
-        *reinterpret_cast<uint32_t *>(p.data + (r0 + t) * (p.K / 2) + c0 / 2) = w;
-      }
-      if ((lane & 1u) == 0) p.scales[(r0 / 16) * KB + c0 / 16] = static_cast<uint8_t>(sb);
+      for (int t = 0; t < 16; ++t) *reinterpret_cast<uint32_t *>(p.data + (wr0 + t) * (p.K / 2) + wc0 / 2) = w[t];
+      if ((lane & 1u) == 0) p.scales[(wr0 / 16) * KB + wc0 / 16] = static_cast<uint8_t>(sb);
     }
   }
 }
@@ -378,30 +438,29 @@ template <int ESZ, int MODE, bool RHT, bool B2D, bool PASS1, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kColCols * (kColTokens / 2)];
   __shared__ __attribute__((aligned(16))) uint8_t lds_scales[kColCols * (kColTokens / 16)];
-  float ts = 0.0f;
-  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out);
   const uint32_t ti = threadIdx.x >> 4;  // token group (16 tokens)
   const uint32_t tj = threadIdx.x & 15;  // column group (8 columns)
   const int64_t KB = p.K / 16;
   uint32_t mx = 0;
-  for (uint32_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+  Raw8<ESZ> v[16];
+  int64_t K0 = 0, R0 = 0, kk = 0, rr = 0;
+  bool valid = false;
+  auto locate = [&](uint32_t tile) {
     const uint32_t tk = fdiv(tile, p.ntr);
-    const uint32_t tr = tile - tk * p.ntr.d;
-    const int64_t K0 = static_cast<int64_t>(tk) * kColTokens;
-    const int64_t R0 = static_cast<int64_t>(tr) * kColCols;
-    const int64_t kk = K0 + 16 * ti;
-    const int64_t rr = R0 + 8 * tj;
-    const bool valid = kk < p.K && rr < p.R;  // K % 16 == 0 and R % 8 == 0
-    Raw8<ESZ> v[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      if (valid) {
-        v[t] = load8<ESZ>(p.x + (kk + t) * p.ldx_bytes + rr * ESZ);
-      } else {
-#pragma unroll
-        for (int i = 0; i < ESZ / 2; ++i) v[t].v[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    K0 = static_cast<int64_t>(tk) * kColTokens;
+    R0 = static_cast<int64_t>(tile - tk * p.ntr.d) * kColCols;
+    kk = K0 + 16 * ti;
+    rr = R0 + 8 * tj;
+    valid = kk < p.K && rr < p.R;  // K % 16 == 0 and R % 8 == 0
+  };
+  uint32_t tile = blockIdx.x;
+  if (tile < p.ntiles) {
+    locate(tile);
+    load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+  }
+  float ts = 0.0f;
+  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out);
+  for (; tile < p.ntiles; tile += gridDim.x) {
     if constexpr (PASS1) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -410,6 +469,10 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
         for (int t = 0; t < 16; ++t) u[t] = raw8_elem<ESZ>(v[t], c);
         if constexpr (RHT) rht16(u, p.sign_word);
         mx = max(mx, __float_as_uint(block_absmax(u)));
+      }
+      if (tile + gridDim.x < p.ntiles) {
+        locate(tile + gridDim.x);
+        load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
       }
       continue;
     }
@@ -442,15 +505,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       }
       uint32_t sb, w0, w1;
       if constexpr (B2D) {
-        uint32_t cc[16];
-        block_codes<kRNE>(u, e2d, i0, 0u, 0u, 0u, cc);
-        w0 = 0u;
-        w1 = 0u;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          w0 |= cc[t] << (4 * t);
-          w1 |= cc[8 + t] << (4 * t);
-        }
+        block_words<kRNE>(u, e2d, i0, 0u, 0u, 0u, w0, w1);
         sb = sb2d;
       } else {
         encode_block<MODE>(u, block_absmax(u), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
@@ -460,6 +515,12 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       const uint32_t rho = 8 * tj + c;
       *reinterpret_cast<uint2 *>(lds_codes + rho * (kColTokens / 2) + 8 * (ti ^ tj)) = make_uint2(w0, w1);
       lds_scales[rho * (kColTokens / 16) + ti] = static_cast<uint8_t>(sb);
+    }
+    const int64_t tK0 = K0, tR0 = R0;
+    // the next tile's loads go out before this tile's output leaves LDS
+    if (tile + gridDim.x < p.ntiles) {
+      locate(tile + gridDim.x);
+      load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
     }
     __syncthreads();
     // codes: 128 rows x 128 B; 8 lanes per row, 16 B each
@@ -471,8 +532,8 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       const uint32_t p0 = (2 * s) ^ sw;
       uint4 val = *reinterpret_cast<const uint4 *>(lds_codes + rho * (kColTokens / 2) + 8 * (p0 & ~1u));
       if (p0 & 1u) val = make_uint4(val.z, val.w, val.x, val.y);
-      const int64_t row = R0 + rho;
-      const int64_t k0 = K0 + 32 * s;  // first token of this 16-byte segment
+      const int64_t row = tR0 + rho;
+      const int64_t k0 = tK0 + 32 * s;  // first token of this 16-byte segment
       if (row < p.R && k0 < p.K) {
         uint8_t *dst = p.data + row * (p.K / 2) + k0 / 2;
         if (ALIGNED) {
@@ -486,15 +547,15 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     if constexpr (!B2D) {
       if (threadIdx.x < kColCols) {
         const uint32_t rho = threadIdx.x;
-        const int64_t row = R0 + rho;
+        const int64_t row = tR0 + rho;
         if (row < p.R) {
-          uint8_t *dst = p.scales + row * KB + K0 / 16;
-          const uint8_t *src = lds_scales + rho * (kColTokens / 16);
+          uint8_t *dst = p.scales + row * KB + tK0 / 16;
+          const uint8_t *srcs = lds_scales + rho * (kColTokens / 16);
           if (ALIGNED) {
-            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(srcs);
           } else {
             for (int q = 0; q < kColTokens / 16; ++q)
-              if (K0 / 16 + q < KB) dst[q] = src[q];
+              if (tK0 / 16 + q < KB) dst[q] = srcs[q];
           }
         }
       }
@@ -503,6 +564,8 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   }
   if constexpr (PASS1) write_partial(mx, p.partial_out);
 }
+
+__global__ void zero_ts_kernel(float *ts) { *ts = 0.0f; }
 
 // ---- host-side dispatch -------------------------------------------------------------------------------
 uint32_t clamp_grid(uint64_t want, uint64_t cap) {
@@ -542,15 +605,15 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint64_t row_bytes = static_cast<uint64_t>(a.cols) * ESZ;
     const uint32_t cpr = static_cast<uint32_t>(row_bytes / 16);
     const uint64_t total = static_cast<uint64_t>(a.rows) * cpr;
-    nparts = clamp_grid((total + 4 * kThreads - 1) / (4 * kThreads), kMaxParts);
+    nparts = clamp_grid((total + 8 * kThreads - 1) / (8 * kThreads), kPass1Parts);
     AmaxArgs am{x, ldx_bytes, static_cast<uint32_t>(total), make_fastdiv(cpr > 0 ? cpr : 1),
                 static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace};
     hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts), dim3(kThreads), 0, a.stream, am);
   } else if (!colwise) {
-    nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kMaxParts);
+    nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kPass1Parts);
     hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, true>), dim3(nparts), dim3(kThreads), 0, a.stream, ra);
   } else {
-    nparts = clamp_grid(col_tiles, kMaxParts);
+    nparts = clamp_grid(col_tiles, kPass1Parts);
     hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false>), dim3(nparts), dim3(kThreads), 0, a.stream, ca);
   }
   hipError_t err = hipGetLastError();
@@ -559,32 +622,33 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   // ---- pass 2
   if (!colwise && !b2d) {
     ra.nparts = nparts;
-    const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, 1u << 30);
+    const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, kPass2Grid);
+    const dim3 g(grid), blk(kThreads);
     if (a.rht) {
       if (mode == kSR)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, true, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, true, false>), g, blk, 0, a.stream, ra);
       else if (mode == kFourOverSix)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, true, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, true, false>), g, blk, 0, a.stream, ra);
       else
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, false>), g, blk, 0, a.stream, ra);
     } else {
       if (mode == kSR)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, false, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, false, false>), g, blk, 0, a.stream, ra);
       else if (mode == kFourOverSix)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, false, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, false, false>), g, blk, 0, a.stream, ra);
       else
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, false, false>), dim3(grid), dim3(kThreads), 0, a.stream, ra);
+        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, false, false>), g, blk, 0, a.stream, ra);
     }
   } else if (!colwise && b2d) {
     const uint32_t nseg = static_cast<uint32_t>((a.K + 511) / 512);
     Row2dArgs r2{x, ldx_bytes, static_cast<uint32_t>((a.R / 16) * nseg), make_fastdiv(nseg), a.K, a.workspace, nparts,
                  a.data, a.scales, a.ts};
-    const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, 1u << 30);
+    const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid);
     hipLaunchKernelGGL(row2d_kernel<ESZ>, dim3(grid), dim3(kThreads), 0, a.stream, r2);
   } else {
     ca.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
-    const dim3 grid(col_tiles), block(kThreads);
+    const dim3 grid(clamp_grid(col_tiles, kPass2Grid)), block(kThreads);
 #define NVFP4_COL(MODE_, RHT_, B2D_)                                                                        \
   do {                                                                                                     \
     if (aligned)                                                                                           \
@@ -610,8 +674,6 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   }
   return hipGetLastError();
 }
-
-__global__ void zero_ts_kernel(float *ts) { *ts = 0.0f; }
 
 }  // namespace
 
