@@ -74,47 +74,62 @@ __device__ __forceinline__ half8 decode8(uint32_t w, uint32_t s2bits) {
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Per-thread staging registers for one K step of one operand: 4 x 16 B of codes, 8 scale bytes.
+// Per-thread staging registers for one K step of one operand: 4 x 16 B of codes, 8 scale bytes,
+// and which of the four code chunks / the scale row lie inside the operand.
 struct Stage {
   uint4 code[4];
   uint32_t sc_lo, sc_hi;
+  uint32_t valid;  // bits 0..3: code chunks, bit 4: scale row
 };
 
 // Global -> registers for rows [row0, row0 + 256) of an operand with valid rows below rows_end.
-template <bool B2D>
+// FULL (K % 128 == 0): every step is whole, so the loads are unconditional: out-of-range rows read
+// a clamped (valid) row and are zeroed when staged into LDS; no branch separates a load from its
+// use, so all loads of a step stay in flight together.
+template <bool B2D, bool FULL>
 __device__ __forceinline__ void load_stage(Stage &st, const uint8_t *__restrict__ data,
                                            const uint8_t *__restrict__ scales, int64_t row0, int64_t rows_end,
                                            int64_t K, int64_t kt) {
   const int64_t row_bytes = K / 2, KB = K / 16;
   const int64_t kb0 = kt * BKB;  // byte offset of this step within a row
+  st.valid = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t c = threadIdx.x + kThreads * i;
     const int64_t r = row0 + (c >> 2);
     const int64_t off = kb0 + 16 * (c & 3);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < rows_end) {
-      const uint8_t *src = data + r * row_bytes + off;
-      if (off + 16 <= row_bytes) {
-        v = *reinterpret_cast<const uint4 *>(src);
-      } else if (off + 8 <= row_bytes) {
-        const uint2 h = *reinterpret_cast<const uint2 *>(src);
-        v = make_uint4(h.x, h.y, 0, 0);
+    if constexpr (FULL) {
+      const int64_t rc = r < rows_end ? r : rows_end - 1;
+      st.code[i] = *reinterpret_cast<const uint4 *>(data + rc * row_bytes + off);
+      st.valid |= (r < rows_end ? 1u : 0u) << i;
+    } else {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < rows_end) {
+        const uint8_t *src = data + r * row_bytes + off;
+        if (off + 16 <= row_bytes) {
+          v = *reinterpret_cast<const uint4 *>(src);
+        } else if (off + 8 <= row_bytes) {
+          const uint2 h = *reinterpret_cast<const uint2 *>(src);
+          v = make_uint4(h.x, h.y, 0, 0);
+        }
       }
+      st.code[i] = v;
+      st.valid |= 1u << i;
     }
-    st.code[i] = v;
   }
   // scales: thread t -> row t, 8 bytes = blocks [8 kt, 8 kt + 8)
   const int64_t r = row0 + threadIdx.x;
-  uint32_t lo = 0, hi = 0;
-  if (r < rows_end) {
-    const uint8_t *src = scales + (B2D ? (r / 16) * KB : r * KB) + 8 * kt;
-    const int64_t nb = KB - 8 * kt;  // blocks left in the row
-    if (nb >= 8 && ((reinterpret_cast<uintptr_t>(src) & 7u) == 0)) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(src);
-      lo = v.x;
-      hi = v.y;
-    } else {
+  if constexpr (FULL) {
+    const int64_t rc = r < rows_end ? r : rows_end - 1;
+    const uint2 v = *reinterpret_cast<const uint2 *>(scales + (B2D ? (rc / 16) * KB : rc * KB) + 8 * kt);
+    st.sc_lo = v.x;
+    st.sc_hi = v.y;
+    st.valid |= (r < rows_end ? 1u : 0u) << 4;
+  } else {
+    uint32_t lo = 0, hi = 0;
+    if (r < rows_end) {
+      const uint8_t *src = scales + (B2D ? (r / 16) * KB : r * KB) + 8 * kt;
+      const int64_t nb = KB - 8 * kt;  // blocks left in the row
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t b = j < nb ? src[j] : 0u;
@@ -124,9 +139,10 @@ __device__ __forceinline__ void load_stage(Stage &st, const uint8_t *__restrict_
           hi |= b << (8 * (j - 4));
       }
     }
+    st.sc_lo = lo;
+    st.sc_hi = hi;
+    st.valid |= 1u << 4;
   }
-  st.sc_lo = lo;
-  st.sc_hi = hi;
 }
 
 // Registers -> LDS stage (codes swizzled, scales converted to fp16 pairs).
@@ -135,18 +151,20 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint8_t *codes, uin
   for (int i = 0; i < 4; ++i) {
     const uint32_t c = threadIdx.x + kThreads * i;
     const uint32_t r = c >> 2, ch = c & 3;
-    *reinterpret_cast<uint4 *>(codes + r * BKB + 16 * (ch ^ ((r >> 1) & 3))) = st.code[i];
+    const uint4 v = ((st.valid >> i) & 1u) ? st.code[i] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4 *>(codes + r * BKB + 16 * (ch ^ ((r >> 1) & 3))) = v;
   }
   const uint32_t r = threadIdx.x;
+  const uint32_t lo = ((st.valid >> 4) & 1u) ? st.sc_lo : 0u, hi = ((st.valid >> 4) & 1u) ? st.sc_hi : 0u;
   uint4 h0, h1;  // blocks 0..3 and 4..7
-  h0.x = scale_pair(st.sc_lo & 0xFF);
-  h0.y = scale_pair((st.sc_lo >> 8) & 0xFF);
-  h0.z = scale_pair((st.sc_lo >> 16) & 0xFF);
-  h0.w = scale_pair(st.sc_lo >> 24);
-  h1.x = scale_pair(st.sc_hi & 0xFF);
-  h1.y = scale_pair((st.sc_hi >> 8) & 0xFF);
-  h1.z = scale_pair((st.sc_hi >> 16) & 0xFF);
-  h1.w = scale_pair(st.sc_hi >> 24);
+  h0.x = scale_pair(lo & 0xFF);
+  h0.y = scale_pair((lo >> 8) & 0xFF);
+  h0.z = scale_pair((lo >> 16) & 0xFF);
+  h0.w = scale_pair(lo >> 24);
+  h1.x = scale_pair(hi & 0xFF);
+  h1.y = scale_pair((hi >> 8) & 0xFF);
+  h1.z = scale_pair((hi >> 16) & 0xFF);
+  h1.w = scale_pair(hi >> 24);
   const uint32_t sw = (r >> 2) & 1;
   *reinterpret_cast<uint4 *>(scales + r * 32 + 16 * sw) = h0;
   *reinterpret_cast<uint4 *>(scales + r * 32 + 16 * (1 ^ sw)) = h1;
@@ -159,7 +177,7 @@ __device__ __forceinline__ int32_t xcd_tile(int32_t wg, int32_t total) {
   return (wg & 7) * (total >> 3) + (wg >> 3);
 }
 
-template <bool OUT_BF16, bool A2D, bool B2D>
+template <bool OUT_BF16, bool A2D, bool B2D, bool FULL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
 
@@ -202,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
 
   Stage sa, sb;
   if (KT > 0) {
-    load_stage<A2D>(sa, p.a_data, p.a_scales, m0, row_end, p.K, 0);
-    load_stage<B2D>(sb, b_data, b_scales, n0, p.N, p.K, 0);
+    load_stage<A2D, FULL>(sa, p.a_data, p.a_scales, m0, row_end, p.K, 0);
+    load_stage<B2D, FULL>(sb, b_data, b_scales, n0, p.N, p.K, 0);
     store_stage(sa, smem, smem + 2 * kCodeBytes);
     store_stage(sb, smem + kCodeBytes, smem + 2 * kCodeBytes + kScaleBytes);
   }
@@ -212,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
   for (int64_t kt = 0; kt < KT; ++kt) {
     const bool more = kt + 1 < KT;
     if (more) {
-      load_stage<A2D>(sa, p.a_data, p.a_scales, m0, row_end, p.K, kt + 1);
-      load_stage<B2D>(sb, b_data, b_scales, n0, p.N, p.K, kt + 1);
+      load_stage<A2D, FULL>(sa, p.a_data, p.a_scales, m0, row_end, p.K, kt + 1);
+      load_stage<B2D, FULL>(sb, b_data, b_scales, n0, p.N, p.K, kt + 1);
     }
     const uint8_t *stage = smem + (kt & 1) * kStageBytes;
     const uint8_t *a_codes = stage, *b_codes = stage + kCodeBytes;
@@ -233,9 +251,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
       as4[f] = *reinterpret_cast<const uint4 *>(a_sc + ra * 32 + 16 * (h ^ ((ra >> 2) & 1)));
       bs4[f] = *reinterpret_cast<const uint4 *>(b_sc + rb * 32 + 16 * (h ^ ((rb >> 2) & 1)));
     }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      half8 af[4], bf[4];
+    // decode sub-step m + 1 while the 16 MFMAs of sub-step m run; the scheduling barriers ask for
+    // one MFMA followed by four decode instructions, so the matrix pipe never waits on a long run of
+    // VALU work (one wave per SIMD issues in order)
+    auto decode_step = [&](int m, half8 (&af)[4], half8 (&bf)[4]) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const uint4 &wa = ac[f][m >> 2];
@@ -247,11 +266,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
         af[f] = decode8(da, sa2);
         bf[f] = decode8(db, sb2);
       }
+    };
+    half8 afc[4], bfc[4];
+    decode_step(0, afc, bfc);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      half8 afn[4], bfn[4];
+      if (m < 7) decode_step(m + 1, afn, bfn);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afc[i], bfc[j], acc[i][j], 0, 0, 0);
+      if (m < 7) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          afc[f] = afn[f];
+          bfc[f] = bfn[f];
+        }
+      }
     }
     if (more) {
       uint8_t *nxt = smem + ((kt + 1) & 1) * kStageBytes;
@@ -262,6 +300,248 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
   }
 
   // ---- epilogue: lane holds column l32 of each 32 x 32 tile, rows 8 * (r >> 2) + 4 * h + (r & 3)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn + 32 * j + l32;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= row_end) continue;
+        const float v = acc[i][j][r] * ts;
+        if constexpr (OUT_BF16) {
+          const uint32_t b = __float_as_uint(v);
+          reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] =
+              static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+        } else {
+          reinterpret_cast<float *>(p.c + row * p.ldc * 4)[col] = v;
+        }
+      }
+    }
+}
+
+
+// ---- pipelined kernel (K % 128 == 0) ----------------------------------------------------------------
+// Same tile and wave layout as gemm_kernel, but the operands reach LDS through direct global->LDS
+// loads (global_load_lds: lane l of an instruction writes 16 B at the LDS base + 16 l, so the XOR
+// swizzle is applied by choosing which global chunk each lane fetches) into a three-stage ring, two
+// K steps ahead of the math.  Scale bytes are staged raw and turned into fp16 pairs when a wave reads
+// its fragments.  The per-step barrier sits after sub-step 4, once every wave holds the step's
+// codes in registers; the next step's first codes and scales are read and decoded under the last
+// MFMAs of the current step, so the matrix pipe does not drain between steps.  Rows beyond the
+// operand read a clamped valid row: their products only reach outputs that are never stored.
+constexpr int kPipeStages = 3;
+constexpr int kPA = 0, kPB = 16384, kPSA = 32768, kPSB = 34816, kPStage = 36864;  // stage layout (bytes)
+constexpr int kLoadsPerStage = 12;  // direct loads issued per lane per stage
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+
+__device__ __forceinline__ void lds_load16(const uint8_t *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const uint8_t *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) only (expcnt / lgkmcnt left alone); gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void issue_stage(uint8_t *stage, const uint8_t *__restrict__ a_data,
+                                            const uint8_t *__restrict__ a_sc, int64_t m0, int64_t m_end,
+                                            const uint8_t *__restrict__ b_data, const uint8_t *__restrict__ b_sc,
+                                            int64_t n0, int64_t n_end, int64_t K, int64_t kt, uint32_t wave,
+                                            uint32_t lane) {
+  const int64_t row_bytes = K / 2, KB = K / 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t R = 64 * wave + 16 * i + (lane >> 2);  // row within the tile
+    const uint32_t c = (lane & 3) ^ ((R >> 1) & 3);       // logical chunk stored at position lane & 3
+    const int64_t ra = min(m0 + R, m_end - 1), rb = min(n0 + R, n_end - 1);
+    lds_load16(a_data + ra * row_bytes + kt * BKB + 16 * c, stage + kPA + (64 * wave + 16 * i) * BKB);
+    lds_load16(b_data + rb * row_bytes + kt * BKB + 16 * c, stage + kPB + (64 * wave + 16 * i) * BKB);
+  }
+  // scales [256 rows][8 B] per operand: waves 0-1 stage A's, waves 2-3 B's, 64 dwords per load
+  const bool is_a = wave < 2;
+  const uint8_t *sc = is_a ? a_sc : b_sc;
+  const int64_t r0 = is_a ? m0 : n0, r_end = is_a ? m_end : n_end;
+  const bool two_d = is_a ? A2D : B2D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t j = 4 * (wave & 1) + i;
+    const int64_t r = min(r0 + 32 * j + (lane >> 1), r_end - 1);
+    lds_load4(sc + (two_d ? (r / 16) * KB : r * KB) + 8 * kt + 4 * (lane & 1),
+              stage + (is_a ? kPSA : kPSB) + 256 * j);
+  }
+}
+
+// Four E4M3 bytes -> four fp16 pairs (S, S).
+__device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
+  const uint32_t lo = __builtin_amdgcn_perm(w, w, 0x01010000u);  // b0 b0 b1 b1
+  const uint32_t hi = __builtin_amdgcn_perm(w, w, 0x03030202u);  // b2 b2 b3 b3
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+  return r;
+}
+
+template <bool OUT_BF16, bool A2D, bool B2D>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPipeStages * kPStage];
+
+  const int32_t tile = xcd_tile(blockIdx.x, p.total_tiles);
+  int32_t g = 0;
+  while (g + 1 < p.groups && p.tile_begin[g + 1] <= tile) ++g;
+  const int32_t local = tile - p.tile_begin[g];
+  const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
+  int32_t tm, tn;
+  {
+    const int32_t band = 8;
+    const int32_t per_band = band * p.tiles_n;
+    const int32_t bi = local / per_band, rem = local - bi * per_band;
+    const int32_t rows_in_band = min(band, tiles_m_g - bi * band);
+    tn = rem / rows_in_band;
+    tm = bi * band + (rem - tn * rows_in_band);
+  }
+  const int64_t row_end = p.row_begin[g + 1];
+  const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
+  const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
+  const float ts = *p.a_ts * p.b_ts[p.group_base + g];
+  const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t KT = p.K / 128;
+
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  const uint32_t h = lane >> 5, l32 = lane & 31u;
+  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto stage_ptr = [&](int64_t kt) { return smem + (kt % kPipeStages) * kPStage; };
+  // LDS byte offsets of this lane's fragment rows
+  uint32_t offA[4], offB[4], swA[4], swB[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const uint32_t ra = wm + 32 * f + l32, rb = wn + 32 * f + l32;
+    offA[f] = ra * BKB;
+    offB[f] = rb * BKB;
+    swA[f] = (ra >> 1) & 3;
+    swB[f] = (rb >> 1) & 3;
+  }
+  auto read_chunk = [&](const uint8_t *st, uint32_t q, uint4 (&ca)[4], uint4 (&cb)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      ca[f] = *reinterpret_cast<const uint4 *>(st + kPA + offA[f] + 16 * ((2 * h + q) ^ swA[f]));
+      cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + offB[f] + 16 * ((2 * h + q) ^ swB[f]));
+    }
+  };
+  auto read_scales = [&](const uint8_t *st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      sa[f] = *reinterpret_cast<const uint32_t *>(st + kPSA + (wm + 32 * f + l32) * 8 + 4 * h);
+      sb[f] = *reinterpret_cast<const uint32_t *>(st + kPSB + (wn + 32 * f + l32) * 8 + 4 * h);
+    }
+  };
+
+  // ---- prologue: stages 0 and 1 in flight, stage 0 read and its first sub-step decoded
+  issue_stage<A2D, B2D>(stage_ptr(0), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K, 0, wave, lane);
+  if (KT > 1)
+    issue_stage<A2D, B2D>(stage_ptr(1), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K, 1, wave, lane);
+  if (KT > 1)
+    wait_vmcnt<kLoadsPerStage>();
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+
+  uint4 ca0[4], cb0[4], ca1[4], cb1[4];  // chunk 0 / chunk 1 codes of the current step
+  uint4 psa[4], psb[4];                   // fp16 scale pairs of the current step (blocks 4h..4h+3)
+  {
+    uint32_t rsa[4], rsb[4];
+    read_chunk(stage_ptr(0), 0, ca0, cb0);
+    read_scales(stage_ptr(0), rsa, rsb);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      psa[f] = scale_pairs4(rsa[f]);
+      psb[f] = scale_pairs4(rsb[f]);
+    }
+  }
+  auto pick = [](const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+  half8 afc[4], bfc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    afc[f] = decode8(ca0[f].x, psa[f].x);
+    bfc[f] = decode8(cb0[f].x, psb[f].x);
+  }
+
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    const bool has_next = kt + 1 < KT;
+    if (kt + 2 < KT)
+      issue_stage<A2D, B2D>(stage_ptr(kt + 2), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K,
+                            kt + 2, wave, lane);
+    read_chunk(stage_ptr(kt), 1, ca1, cb1);
+    uint32_t nsa[4], nsb[4];  // next step's raw scale bytes
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      half8 afn[4], bfn[4];
+      if (m < 7) {
+        const int mn = m + 1;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const uint32_t da = mn < 4 ? pick(ca0[f], mn) : pick(ca1[f], mn - 4);
+          const uint32_t db = mn < 4 ? pick(cb0[f], mn) : pick(cb1[f], mn - 4);
+          afn[f] = decode8(da, pick(psa[f], mn >> 1));
+          bfn[f] = decode8(db, pick(psb[f], mn >> 1));
+        }
+      } else if (has_next) {
+        // the current step's scales and chunk 0 are dead: ca0 / cb0 already hold the next step's
+        // chunk 0 (read after the barrier below), and its scale pairs replace psa / psb
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          psa[f] = scale_pairs4(nsa[f]);
+          psb[f] = scale_pairs4(nsb[f]);
+          afn[f] = decode8(ca0[f].x, psa[f].x);
+          bfn[f] = decode8(cb0[f].x, psb[f].x);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afc[i], bfc[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        afc[f] = afn[f];
+        bfc[f] = bfn[f];
+      }
+      if (m == 4 && has_next) {
+        // every wave has consumed this step's LDS data (chunk 0 was last decoded for sub-step 3,
+        // chunk 1 is in registers since sub-step 4): stage kt may now be overwritten, and stage
+        // kt + 1 is complete once each lane's own loads for it are
+        if (kt + 2 < KT)
+          wait_vmcnt<kLoadsPerStage>();
+        else
+          wait_vmcnt<0>();
+        __syncthreads();
+        read_chunk(stage_ptr(kt + 1), 0, ca0, cb0);
+        read_scales(stage_ptr(kt + 1), nsa, nsb);
+      }
+    }
+  }
+
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -321,8 +601,16 @@ hipError_t launch_gemm(const GemmArgs &a) {
     p.total_tiles = tiles;
     if (tiles == 0) continue;  // K == 0 still launches: the K loop is empty and C = 0
     const bool bf16 = a.c_dtype == 1;
-#define NVFP4_GEMM(OB, A2, B2) \
-  hipLaunchKernelGGL((gemm_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
+    // whole K steps and 8-byte aligned scale rows: branch-free loads
+    const bool full = (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0;
+#define NVFP4_GEMM(OB, A2, B2)                                                                            \
+  do {                                                                                                   \
+    if (full)                                                                                            \
+      hipLaunchKernelGGL((gemm_pipe_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p);   \
+    else                                                                                                 \
+      hipLaunchKernelGGL((gemm_kernel<OB, A2, B2, false>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
+  } while (0)
     if (bf16) {
       if (a.a_2d && a.b_2d) NVFP4_GEMM(true, true, true);
       else if (a.a_2d) NVFP4_GEMM(true, true, false);

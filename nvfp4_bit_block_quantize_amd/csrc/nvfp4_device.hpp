@@ -170,12 +170,4 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Largest |x| of the whole tensor from the pass-1 partial maxima (float bits of non-negative
-// values compare like unsigned integers).  Called by every wave; no barrier.
-__device__ __forceinline__ float tensor_amax(const uint32_t *__restrict__ partial, uint32_t nparts) {
-  uint32_t m = 0;
-  for (uint32_t i = threadIdx.x & 63u; i < nparts; i += 64u) m = max(m, partial[i]);
-  return __uint_as_float(wave_max_u32(m));
-}
-
 }  // namespace nvfp4

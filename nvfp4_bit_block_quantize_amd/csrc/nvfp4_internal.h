@@ -8,7 +8,7 @@
 namespace nvfp4 {
 
 // Upper bound on the number of amax-pass workgroups; the workspace holds one partial maximum each.
-constexpr uint32_t kMaxParts = 1024;
+constexpr uint32_t kMaxParts = 4096;
 
 struct QuantArgs {
   const void *x;

@@ -4,11 +4,11 @@
 //   pass 1  tensor amax: every workgroup writes the largest |y| it saw to workspace[blockIdx.x]
 //           (plain tensors: amax_kernel; with the Hadamard transform the maximum is taken over the
 //           transformed values, by the pass-2 kernels compiled with PASS1 = true);
-//   pass 2  every wave reduces the partial maxima itself (no atomics, no zero-initialised memory),
+//   pass 2  every workgroup reduces the partial maxima itself (no atomics, no zeroed memory),
 //           derives ts = amax / 2688, and encodes its blocks: block amax -> E4M3 scale -> E2M1
 //           codes (nearest-even, stochastic or Four-over-Six) -> packed nibbles.
 // Pass-2 grids are persistent (a few workgroups per CU, grid-stride over the work) so that the
-// per-wave partial reduction is paid a few times per CU, and each lane issues the loads of its
+// partial reduction is paid a few times per CU, and each lane issues the loads of its
 // next block before it encodes the current one.
 //
 // Nearest-even encoding uses v_cvt_scalef32_pk_fp4_f32 with scale 1.0: two fp32 values -> two
@@ -31,7 +31,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kPass1Parts = 512;  // amax-pass workgroups (<= kMaxParts)
+constexpr uint32_t kPass1Parts = 4096; // amax-pass workgroups (<= kMaxParts)
 constexpr uint32_t kPass2Grid = 2048;  // persistent pass-2 workgroups (8 per CU)
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -213,11 +213,20 @@ __device__ __forceinline__ void write_partial(uint32_t m, uint32_t *__restrict__
   }
 }
 
-// Every wave: tensor amax from the partials, ts = amax / 2688; block 0 publishes ts.
+// Tensor amax from the pass-1 partial maxima (float bits of non-negative values compare like
+// unsigned integers), reduced once per workgroup; ts = amax / 2688; workgroup 0 publishes ts.
+// Called by every thread of the workgroup (contains a barrier).
 __device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ partial, uint32_t nparts,
                                               float *__restrict__ ts_out) {
-  const float A = tensor_amax(partial, nparts);
-  const float ts = A / 2688.0f;
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partial[i]);
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+#pragma unroll
+  for (uint32_t w = 0; w < kThreads / 64; ++w) m = max(m, red[w]);
+  const float ts = __uint_as_float(m) / 2688.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
   return ts;
 }
