@@ -7,7 +7,7 @@ nvfp4_quantize(W) (16x16 tiles) + nvfp4_gemm(X_q, W_q) -> Y [8192 x 14336] bf16,
 Inputs are generated once and resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step
-time); the components object carries the quantize GB/s (algorithmic bytes: both passes' reads plus
+time, the step replayed as one HIP graph); the components object carries the quantize GB/s (algorithmic bytes: both passes' reads plus
 the codes and scales written) and the GEMM-only TFLOP/s; `roofline` describes the dominant kernel
 (the GEMM) against the MI355X dense fp16 MFMA peak; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
@@ -35,7 +35,7 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=512, help="rows of X and W in the CPU sample")
+    p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
     return p.parse_args()
 
 
@@ -105,22 +105,49 @@ def main():
     def mm():
         nv.nvfp4_gemm(qa, qb, out=y)
 
-    for _ in range(a.warmup):
+    def step():
         q_a(); q_b(); mm()
+
+    for _ in range(a.warmup):
+        step()
     torch.cuda.synchronize()
 
+    # per-kernel times: eager launches bracketed by events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(a.steps):
         e = evs[s]
         e[0].record(); q_a(); e[1].record(); q_b(); e[2].record(); mm(); e[3].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     qa_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
     qb_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
     mm_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
+    y_eager = y.clone()
+
+    # the step as one HIP graph (every library call is capturable: kernels only, no memsets)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm the side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(y, y_eager))
+    if not graph_ok:
+        print(json.dumps({"error": "graph replay differs from eager result"}))
+        sys.exit(1)
+    for _ in range(a.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
     ms_step = wall * 1e3 / a.steps
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (mm_ms * 1e-3) / 1e12
@@ -149,6 +176,7 @@ def main():
             "quantize_algorithmic_bytes": qbytes,
             "gemm_ms": round(mm_ms, 4),
             "gemm_tflops": round(gemm_tflops, 1),
+            "step_timing": "HIP graph replay of quantize(A) + quantize(B) + GEMM; components from eager launches",
         },
         "roofline": {
             "kernel": "nvfp4 gemm",
