@@ -36,6 +36,9 @@ def _args():
     p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run 5 device-to-device copies of MIB MiB (a known-size kernel for scaling "
+                        "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -44,6 +47,30 @@ def quant_bytes(rows, cols, block2d):
     the packed codes and the scale bytes."""
     n = rows * cols
     return n * 2 + n * 2 + n // 2 + (n // 256 if block2d else n // 16)
+
+
+def gemm_source_digest():
+    """sha256 over the GEMM kernel sources (the counters below are only valid for this source)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "nvfp4_device.hpp"):
+        with open(os.path.join(ROOT, "nvfp4_bit_block_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled
+    by the copy-kernel calibration; None when the summary is missing or was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "gemm_fprop8b_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != gemm_source_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def main():
@@ -61,6 +88,15 @@ def main():
     nv.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+        return
 
     if a.workload == "fprop8b":
         x_cpu, w_cpu = synth.fprop8b(0)
@@ -185,7 +221,7 @@ def main():
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_gemm_traffic(),
         },
     }
     if not a.no_cpu:
