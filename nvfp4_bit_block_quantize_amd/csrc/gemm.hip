@@ -53,6 +53,7 @@ struct GemmKArgs {
   int64_t b_group_data;    // bytes between consecutive groups' B codes
   int64_t b_group_scales;  // bytes between consecutive groups' B scales
   int32_t group_base;      // index of the first group of this launch (for b offsets)
+  int32_t vec_store;       // C rows allow 8-byte (bf16) / 16-byte (fp32) stores of 4 columns
   int64_t row_begin[kMaxGroupsPerLaunch + 1];  // A rows of each group
   int32_t tile_begin[kMaxGroupsPerLaunch + 1]; // first tile of each group (prefix sums)
 };
@@ -324,20 +325,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
 
 
 // ---- pipelined kernel (K % 128 == 0) ----------------------------------------------------------------
-// Same tile and wave layout as gemm_kernel, but the operands reach LDS through direct global->LDS
-// loads (global_load_lds: lane l of an instruction writes 16 B at the LDS base + 16 l, so the XOR
-// swizzle is applied by choosing which global chunk each lane fetches) into a three-stage ring, two
-// K steps ahead of the math.  Scale bytes are staged raw and turned into fp16 pairs when a wave reads
-// its fragments.  The per-step barrier sits after sub-step 4, once every wave holds the step's
-// codes in registers; the next step's first codes and scales are read and decoded under the last
-// MFMAs of the current step, so the matrix pipe does not drain between steps.  Rows beyond the
-// operand read a clamped valid row: their products only reach outputs that are never stored.
-constexpr int kPipeStages = 3;
+// Same tile and wave layout as gemm_kernel.  The operands reach LDS through direct global->LDS loads
+// (global_load_lds: lane l of an instruction writes 16 B at the LDS base + 16 l, so the swizzle is
+// applied by choosing which global chunk each lane fetches) into a ring of three stages, two K steps
+// ahead of the math.  A K step takes its three stages (current, next, refill target) as __restrict__
+// pointers, so the compiler knows that a fragment read does not alias the direct loads in flight to
+// another stage and does not stall on them; the explicit waits before the step's barrier are what
+// order the loads of one step before the reads of the next (for this wave and, through the barrier,
+// for the others).
+// One barrier per step, after sub-step 4: by then every wave holds the step's codes in registers;
+// after it the next step's first codes and scales are read, and decoded under the last MFMAs.
+// The MFMA takes the B fragment as its first operand, so that a lane's accumulators hold four
+// consecutive columns of one row of C, which leave as one 8-byte (bf16) or 16-byte (fp32) store.
+// Rows beyond the operand read a clamped valid row: their products reach only outputs that are never
+// stored.  Steps beyond K re-fetch the last step into a stage that is never consumed.
 constexpr int kPA = 0, kPB = 16384, kPSA = 32768, kPSB = 34816, kPStage = 36864;  // stage layout (bytes)
 constexpr int kLoadsPerStage = 12;  // direct loads issued per lane per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void lds_load16(const uint8_t *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 16, 0, 0);
@@ -346,40 +354,25 @@ __device__ __forceinline__ void lds_load4(const uint8_t *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 4, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) only (expcnt / lgkmcnt left alone); gfx9 encoding.
+// s_waitcnt vmcnt(N) / lgkmcnt(0) only (the other counters left alone); gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <bool A2D, bool B2D>
-__device__ __forceinline__ void issue_stage(uint8_t *stage, const uint8_t *__restrict__ a_data,
-                                            const uint8_t *__restrict__ a_sc, int64_t m0, int64_t m_end,
-                                            const uint8_t *__restrict__ b_data, const uint8_t *__restrict__ b_sc,
-                                            int64_t n0, int64_t n_end, int64_t K, int64_t kt, uint32_t wave,
-                                            uint32_t lane) {
-  const int64_t row_bytes = K / 2, KB = K / 16;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t R = 64 * wave + 16 * i + (lane >> 2);  // row within the tile
-    const uint32_t c = (lane & 3) ^ ((R >> 1) & 3);       // logical chunk stored at position lane & 3
-    const int64_t ra = min(m0 + R, m_end - 1), rb = min(n0 + R, n_end - 1);
-    lds_load16(a_data + ra * row_bytes + kt * BKB + 16 * c, stage + kPA + (64 * wave + 16 * i) * BKB);
-    lds_load16(b_data + rb * row_bytes + kt * BKB + 16 * c, stage + kPB + (64 * wave + 16 * i) * BKB);
-  }
-  // scales [256 rows][8 B] per operand: waves 0-1 stage A's, waves 2-3 B's, 64 dwords per load
-  const bool is_a = wave < 2;
-  const uint8_t *sc = is_a ? a_sc : b_sc;
-  const int64_t r0 = is_a ? m0 : n0, r_end = is_a ? m_end : n_end;
-  const bool two_d = is_a ? A2D : B2D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t j = 4 * (wave & 1) + i;
-    const int64_t r = min(r0 + 32 * j + (lane >> 1), r_end - 1);
-    lds_load4(sc + (two_d ? (r / 16) * KB : r * KB) + 8 * kt + 4 * (lane & 1),
-              stage + (is_a ? kPSA : kPSB) + 256 * j);
-  }
+// Workgroup barrier that the compiler may not move memory accesses across; the caller has issued
+// the waits that make its own LDS traffic complete.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
+
+// Chunk c (16 B) of tile row r is stored at position c ^ swz(r) of its 64-byte row: 8 or 16
+// consecutive rows reading the same chunk touch distinct 16-byte bank groups of a 128- or 256-byte
+// bank line, so a ds_read_b128 of a fragment is conflict-free.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3u; }
 
 // Four E4M3 bytes -> four fp16 pairs (S, S).
 __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
@@ -393,9 +386,20 @@ __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
   return r;
 }
 
+__device__ __forceinline__ uint32_t pick(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// fp32 -> bf16, nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 template <bool OUT_BF16, bool A2D, bool B2D>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPipeStages * kPStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kPStage];
+  uint8_t *const st0 = smem, *const st1 = smem + kPStage;
 
   const int32_t tile = xcd_tile(blockIdx.x, p.total_tiles);
   int32_t g = 0;
@@ -414,72 +418,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
   const int64_t row_end = p.row_begin[g + 1];
   const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
-  const float ts = *p.a_ts * p.b_ts[p.group_base + g];
   const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t KT = p.K / 128;
 
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
 
-  floatx16 acc[4][4];
+  // ---- direct-load sources: 32-bit per-lane offsets (an operand is below 2 GiB) from per-step bases
+  const int64_t row_bytes = p.K / 2, KB = p.K / 16;
+  uint32_t srcA[4], srcB[4], srcS[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  auto stage_ptr = [&](int64_t kt) { return smem + (kt % kPipeStages) * kPStage; };
-  // LDS byte offsets of this lane's fragment rows
-  uint32_t offA[4], offB[4], swA[4], swB[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const uint32_t ra = wm + 32 * f + l32, rb = wn + 32 * f + l32;
-    offA[f] = ra * BKB;
-    offB[f] = rb * BKB;
-    swA[f] = (ra >> 1) & 3;
-    swB[f] = (rb >> 1) & 3;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t R = 64 * wave + 16 * i + (lane >> 2);  // tile row this lane fetches
+    const uint32_t c = (lane & 3) ^ swz(R);               // logical chunk stored at position lane & 3
+    const int64_t ra = min(m0 + R, row_end - 1), rb = min(n0 + R, p.N - 1);
+    srcA[i] = static_cast<uint32_t>(ra * row_bytes + 16 * c);
+    srcB[i] = static_cast<uint32_t>(rb * row_bytes + 16 * c);
   }
-  auto read_chunk = [&](const uint8_t *st, uint32_t q, uint4 (&ca)[4], uint4 (&cb)[4]) {
+  // scales [256 rows][8 B] per operand: waves 0-1 stage A's, waves 2-3 B's, 64 dwords per load
+  const bool is_a = wave < 2;
+  const uint8_t *sc_base = is_a ? p.a_scales : b_scales;
+  {
+    const int64_t r0 = is_a ? m0 : n0, r_end = is_a ? row_end : p.N;
+    const bool two_d = is_a ? A2D : B2D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = min(r0 + 32 * (4 * (wave & 1) + i) + (lane >> 1), r_end - 1);
+      srcS[i] = static_cast<uint32_t>((two_d ? (r / 16) * KB : r * KB) + 4 * (lane & 1));
+    }
+  }
+  const uint32_t lds_codes = 4096 * wave;                                    // + 1024 i
+  const uint32_t lds_sc = (is_a ? kPSA : kPSB) + 1024 * (wave & 1);         // + 256 i
+  auto issue = [&](uint8_t *st, int64_t kt) {
+    const int64_t kc = kt < KT ? kt : KT - 1;
+    const uint8_t *ga = p.a_data + kc * 64, *gb = b_data + kc * 64, *gs = sc_base + kc * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_load16(ga + srcA[i], st + kPA + lds_codes + 1024 * i);
+      lds_load16(gb + srcB[i], st + kPB + lds_codes + 1024 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
+  };
+
+  // ---- fragment reads: lane half h takes codes [64 h, 64 h + 64) of the step, chunk q of its half
+  const uint32_t rdA = (wm + l32) * 64, rdB = (wn + l32) * 64;
+  const uint32_t pos0 = 16 * ((2 * h) ^ swz(l32)), pos1 = 16 * ((2 * h + 1) ^ swz(l32));
+  const uint32_t rsA = kPSA + (wm + l32) * 8 + 4 * h, rsB = kPSB + (wn + l32) * 8 + 4 * h;
+  auto read_chunk = [&](const uint8_t *st, uint32_t pos, uint4 (&ca)[4], uint4 (&cb)[4]) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      ca[f] = *reinterpret_cast<const uint4 *>(st + kPA + offA[f] + 16 * ((2 * h + q) ^ swA[f]));
-      cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + offB[f] + 16 * ((2 * h + q) ^ swB[f]));
+      ca[f] = *reinterpret_cast<const uint4 *>(st + kPA + rdA + 2048 * f + pos);
+      cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + rdB + 2048 * f + pos);
     }
   };
   auto read_scales = [&](const uint8_t *st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      sa[f] = *reinterpret_cast<const uint32_t *>(st + kPSA + (wm + 32 * f + l32) * 8 + 4 * h);
-      sb[f] = *reinterpret_cast<const uint32_t *>(st + kPSB + (wn + 32 * f + l32) * 8 + 4 * h);
+      sa[f] = *reinterpret_cast<const uint32_t *>(st + rsA + 256 * f);
+      sb[f] = *reinterpret_cast<const uint32_t *>(st + rsB + 256 * f);
     }
   };
 
-  // ---- prologue: stages 0 and 1 in flight, stage 0 read and its first sub-step decoded
-  issue_stage<A2D, B2D>(stage_ptr(0), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K, 0, wave, lane);
-  if (KT > 1)
-    issue_stage<A2D, B2D>(stage_ptr(1), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K, 1, wave, lane);
-  if (KT > 1)
-    wait_vmcnt<kLoadsPerStage>();
-  else
-    wait_vmcnt<0>();
-  __syncthreads();
+  floatx16 acc[4][4];  // [B fragment j][A fragment i]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
+  // ---- prologue: steps 0 and 1 in flight, step 0's first chunk read and its sub-step 0 decoded
+  issue(st0, 0);
+  issue(st1, 1);
+  wait_vmcnt<kLoadsPerStage>();
+  lds_barrier();
   uint4 ca0[4], cb0[4], ca1[4], cb1[4];  // chunk 0 / chunk 1 codes of the current step
   uint4 psa[4], psb[4];                   // fp16 scale pairs of the current step (blocks 4h..4h+3)
   {
     uint32_t rsa[4], rsb[4];
-    read_chunk(stage_ptr(0), 0, ca0, cb0);
-    read_scales(stage_ptr(0), rsa, rsb);
+    read_chunk(st0, pos0, ca0, cb0);
+    read_scales(st0, rsa, rsb);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       psa[f] = scale_pairs4(rsa[f]);
       psb[f] = scale_pairs4(rsb[f]);
     }
   }
-  auto pick = [](const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
   half8 afc[4], bfc[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -487,12 +515,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
     bfc[f] = decode8(cb0[f].x, psb[f].x);
   }
 
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    const bool has_next = kt + 1 < KT;
-    if (kt + 2 < KT)
-      issue_stage<A2D, B2D>(stage_ptr(kt + 2), p.a_data, p.a_scales, m0, row_end, b_data, b_scales, n0, p.N, p.K,
-                            kt + 2, wave, lane);
-    read_chunk(stage_ptr(kt), 1, ca1, cb1);
+  // one K step out of stage S: the 8 sub-steps of 16 codes, 16 MFMAs each
+  auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt, int64_t kt) {
+    issue(tgt, kt + 2);
+    read_chunk(cur, pos1, ca1, cb1);
     uint32_t nsa[4], nsb[4];  // next step's raw scale bytes
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -506,9 +532,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
           afn[f] = decode8(da, pick(psa[f], mn >> 1));
           bfn[f] = decode8(db, pick(psb[f], mn >> 1));
         }
-      } else if (has_next) {
-        // the current step's scales and chunk 0 are dead: ca0 / cb0 already hold the next step's
-        // chunk 0 (read after the barrier below), and its scale pairs replace psa / psb
+      } else {
+        // this step's scales and chunk 0 are dead: ca0 / cb0 hold the next step's chunk 0 (read
+        // after the barrier below) and its scale pairs replace psa / psb
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           psa[f] = scale_pairs4(nsa[f]);
@@ -518,50 +544,84 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afc[i], bfc[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfc[j], afc[i], acc[j][i], 0, 0, 0);
+      // one MFMA, then four decode instructions: the matrix pipe is never left behind a long run of
+      // VALU work (a wave issues in order)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         afc[f] = afn[f];
         bfc[f] = bfn[f];
       }
-      if (m == 4 && has_next) {
-        // every wave has consumed this step's LDS data (chunk 0 was last decoded for sub-step 3,
-        // chunk 1 is in registers since sub-step 4): stage kt may now be overwritten, and stage
-        // kt + 1 is complete once each lane's own loads for it are
-        if (kt + 2 < KT)
-          wait_vmcnt<kLoadsPerStage>();
-        else
-          wait_vmcnt<0>();
-        __syncthreads();
-        read_chunk(stage_ptr(kt + 1), 0, ca0, cb0);
-        read_scales(stage_ptr(kt + 1), nsa, nsb);
+      if (m == 4) {
+        // every wave holds this step's codes in registers (chunk 1 since sub-step 3's decode), and
+        // this lane's loads for step kt + 1 have landed: after the barrier the next stage is complete
+        // and this one may be refilled
+        wait_vmcnt<kLoadsPerStage>();
+        wait_lgkmcnt0();
+        lds_barrier();
+        read_chunk(nxt, pos0, ca0, cb0);
+        read_scales(nxt, nsa, nsb);
       }
     }
+  };
+  uint8_t *cur = st0, *nxt = st1, *tgt = smem + 2 * kPStage;
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    step(cur, nxt, tgt, kt);
+    uint8_t *const done = cur;
+    cur = nxt;
+    nxt = tgt;
+    tgt = done;
   }
 
+  // ---- epilogue: lane holds row l32 of each 32 x 32 tile, columns 8 (r >> 2) + 4 h + (r & 3)
+  const float ts = *p.a_ts * p.b_ts[p.group_base + g];
+  constexpr int64_t ES = OUT_BF16 ? 2 : 4;
+  const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
+  if (p.vec_store && m0 + BM <= row_end && n0 + BN <= p.N) {
+    uint8_t *base = p.c + (row0 * p.ldc + col0) * ES;
+    const int64_t row_step = 32 * p.ldc * ES;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn + 32 * j + l32;
-      if (col >= p.N) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= row_end) continue;
-        const float v = acc[i][j][r] * ts;
-        if constexpr (OUT_BF16) {
-          const uint32_t b = __float_as_uint(v);
-          reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] =
-              static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-        } else {
-          reinterpret_cast<float *>(p.c + row * p.ldc * 4)[col] = v;
+        for (int q = 0; q < 4; ++q) {
+          uint8_t *dst = base + i * row_step + (32 * j + 8 * q) * ES;
+          const float v0 = acc[j][i][4 * q] * ts, v1 = acc[j][i][4 * q + 1] * ts;
+          const float v2 = acc[j][i][4 * q + 2] * ts, v3 = acc[j][i][4 * q + 3] * ts;
+          if constexpr (OUT_BF16) {
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+          } else {
+            *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+          }
         }
-      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + 32 * i;
+      if (row >= row_end) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
+          if (col >= p.N) continue;
+          const float v = acc[j][i][r] * ts;
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] = static_cast<uint16_t>(bf16_rne(v));
+          else
+            reinterpret_cast<float *>(p.c + row * p.ldc * 4)[col] = v;
+        }
     }
+  }
 }
 
 }  // namespace
@@ -601,6 +661,8 @@ hipError_t launch_gemm(const GemmArgs &a) {
     p.total_tiles = tiles;
     if (tiles == 0) continue;  // K == 0 still launches: the K loop is empty and C = 0
     const bool bf16 = a.c_dtype == 1;
+    const uintptr_t c_align = bf16 ? 8 : 16;
+    p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % c_align) == 0 && (a.ldc % 4) == 0;
     // whole K steps and 8-byte aligned scale rows: branch-free loads
     const bool full = (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0;
