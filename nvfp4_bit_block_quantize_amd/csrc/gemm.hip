@@ -53,7 +53,7 @@ struct GemmKArgs {
   int64_t b_group_data;    // bytes between consecutive groups' B codes
   int64_t b_group_scales;  // bytes between consecutive groups' B scales
   int32_t group_base;      // index of the first group of this launch (for b offsets)
-  int32_t vec_store;       // C rows allow 8-byte (bf16) / 16-byte (fp32) stores of 4 columns
+  int32_t vec_store;       // C and its rows are 16-byte aligned (row-segment stores)
   int64_t row_begin[kMaxGroupsPerLaunch + 1];  // A rows of each group
   int32_t tile_begin[kMaxGroupsPerLaunch + 1]; // first tile of each group (prefix sums)
 };
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
 // One barrier per step, after sub-step 4: by then every wave holds the step's codes in registers;
 // after it the next step's first codes and scales are read, and decoded under the last MFMAs.
 // The MFMA takes the B fragment as its first operand, so that a lane's accumulators hold four
-// consecutive columns of one row of C, which leave as one 8-byte (bf16) or 16-byte (fp32) store.
+// consecutive columns of one row of C (staged through LDS for whole-row-segment stores).
 // Rows beyond the operand read a clamped valid row: their products reach only outputs that are never
 // stored.  Steps beyond K re-fetch the last step into a stage that is never consumed.
 constexpr int kPA = 0, kPB = 16384, kPSA = 32768, kPSB = 34816, kPStage = 36864;  // stage layout (bytes)
@@ -581,29 +581,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
     tgt = done;
   }
 
-  // ---- epilogue: lane holds row l32 of each 32 x 32 tile, columns 8 (r >> 2) + 4 h + (r & 3)
+  // ---- epilogue: lane holds row l32 of each 32 x 32 tile, columns 8 (r >> 2) + 4 h + (r & 3).
+  // Whole tiles go through LDS, 32 rows of the wave's quarter at a time, so that each store writes
+  // 16 consecutive bytes per lane and four (bf16) or two (fp32) complete 256 / 512-byte row segments
+  // per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row).
   const float ts = *p.a_ts * p.b_ts[p.group_base + g];
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
-  const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
   if (p.vec_store && m0 + BM <= row_end && n0 + BN <= p.N) {
-    uint8_t *base = p.c + (row0 * p.ldc + col0) * ES;
-    const int64_t row_step = 32 * p.ldc * ES;
+    // all waves are done with the stages and the last (re-fetch) loads have landed
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    lds_barrier();
+    constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
+    uint8_t *const region = smem + wave * (32 * ROWB);
+    uint8_t *const gbase = p.c + ((m0 + wm) * p.ldc + n0 + wn) * ES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint8_t *dst = base + i * row_step + (32 * j + 8 * q) * ES;
           const float v0 = acc[j][i][4 * q] * ts, v1 = acc[j][i][4 * q + 1] * ts;
           const float v2 = acc[j][i][4 * q + 2] * ts, v3 = acc[j][i][4 * q + 3] * ts;
           if constexpr (OUT_BF16) {
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+            // v_cvt_pk_bf16_f32: nearest-even, as the integer rounding used elsewhere in this file
+            const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
+            const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
+            const uint32_t c = 4 * j + q;
+            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((c ^ (l32 & 15)) * 16 + 8 * h)) =
+                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
           } else {
-            *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+            const uint32_t c = 8 * j + 2 * q + h;
+            *reinterpret_cast<float4 *>(region + l32 * ROWB + (c ^ (l32 & 31)) * 16) = make_float4(v0, v1, v2, v3);
           }
         }
+      // the wave reads back its own rows (LDS accesses of one wave complete in order)
+#pragma unroll
+      for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
+        const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
+        const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
+        *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * p.ldc * ES + u * 16) = v;
+      }
+    }
   } else {
+    const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = row0 + 32 * i;
@@ -661,8 +682,7 @@ hipError_t launch_gemm(const GemmArgs &a) {
     p.total_tiles = tiles;
     if (tiles == 0) continue;  // K == 0 still launches: the K loop is empty and C = 0
     const bool bf16 = a.c_dtype == 1;
-    const uintptr_t c_align = bf16 ? 8 : 16;
-    p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % c_align) == 0 && (a.ldc % 4) == 0;
+    p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % 16) == 0 && ((a.ldc * (bf16 ? 2 : 4)) % 16) == 0;
     // whole K steps and 8-byte aligned scale rows: branch-free loads
     const bool full = (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0;
