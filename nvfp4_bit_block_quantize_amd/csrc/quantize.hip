@@ -31,7 +31,10 @@ namespace nvfp4 {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kPass1Parts = 4096; // amax-pass workgroups (<= kMaxParts)
+constexpr uint32_t kPass1Parts = 1024; // pass-1 workgroups at most (<= kMaxParts): the partial maxima
+                                       // every pass-2 wave reduces
+constexpr uint32_t kAmaxThreads = 1024; // amax_kernel workgroup: one per CU, 16 waves
+constexpr uint32_t kAmaxParts = 256;
 constexpr uint32_t kPass2Grid = 2048;  // persistent pass-2 workgroups (8 per CU)
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -199,33 +202,31 @@ __device__ __forceinline__ float block_absmax(const float (&y)[16]) {
   return ab;
 }
 
-// Workgroup max of one value per lane -> partial[blockIdx.x] (thread 0).
+// Workgroup max of one value per lane -> partial[blockIdx.x] (thread 0).  NT = threads per group.
+template <uint32_t NT = kThreads>
 __device__ __forceinline__ void write_partial(uint32_t m, uint32_t *__restrict__ partial) {
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[NT / 64];
   m = wave_max_u32(m);
   if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
 #pragma unroll
-    for (uint32_t w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+    for (uint32_t w = 1; w < NT / 64; ++w) r = max(r, red[w]);
     partial[blockIdx.x] = r;
   }
 }
 
 // Tensor amax from the pass-1 partial maxima (float bits of non-negative values compare like
-// unsigned integers), reduced once per workgroup; ts = amax / 2688; workgroup 0 publishes ts.
-// Called by every thread of the workgroup (contains a barrier).
+// unsigned integers), reduced by every wave on its own (at most kPass1Parts values, no barrier);
+// ts = amax / 2688; wave 0 of workgroup 0 publishes ts.
 __device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ partial, uint32_t nparts,
                                               float *__restrict__ ts_out) {
-  __shared__ uint32_t red[kThreads / 64];
+  const uint32_t lane = threadIdx.x & 63u;
   uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partial[i]);
+#pragma unroll 4
+  for (uint32_t i = lane; i < nparts; i += 64) m = max(m, partial[i]);
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-#pragma unroll
-  for (uint32_t w = 0; w < kThreads / 64; ++w) m = max(m, red[w]);
   const float ts = __uint_as_float(m) / 2688.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
   return ts;
@@ -253,9 +254,9 @@ __device__ __forceinline__ void absmax_chunk(const uint4 &v, u16x2 &m2, uint32_t
 }
 
 template <int ESZ>
-__global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs p) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs p) {
   constexpr int U = 8;  // loads in flight per lane
-  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t stride = gridDim.x * kAmaxThreads;
   u16x2 m2 = {0, 0};
   uint32_t m4 = 0;
   auto addr = [&](uint32_t c) -> const uint4 * {
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs p) {
     return reinterpret_cast<const uint4 *>(p.x + static_cast<int64_t>(r) * p.ldx_bytes +
                                            static_cast<int64_t>(c - r * p.cpr.d) * 16);
   };
-  uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+  uint32_t c = blockIdx.x * kAmaxThreads + threadIdx.x;
   for (; c + (U - 1) * stride < p.total_chunks; c += U * stride) {
     uint4 v[U];
 #pragma unroll
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs p) {
   }
   for (; c < p.total_chunks; c += stride) absmax_chunk<ESZ>(*addr(c), m2, m4);
   const uint32_t m = ESZ == 2 ? (static_cast<uint32_t>(max(m2.x, m2.y)) << 16) : m4;
-  write_partial(m, p.partial);
+  write_partial<kAmaxThreads>(m, p.partial);
 }
 
 // ---- ROW mode, 1D blocks ----------------------------------------------------------------------------
@@ -614,10 +615,10 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint64_t row_bytes = static_cast<uint64_t>(a.cols) * ESZ;
     const uint32_t cpr = static_cast<uint32_t>(row_bytes / 16);
     const uint64_t total = static_cast<uint64_t>(a.rows) * cpr;
-    nparts = clamp_grid((total + 8 * kThreads - 1) / (8 * kThreads), kPass1Parts);
+    nparts = clamp_grid((total + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads), kAmaxParts);
     AmaxArgs am{x, ldx_bytes, static_cast<uint32_t>(total), make_fastdiv(cpr > 0 ? cpr : 1),
                 static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace};
-    hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts), dim3(kThreads), 0, a.stream, am);
+    hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts), dim3(kAmaxThreads), 0, a.stream, am);
   } else if (!colwise) {
     nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kPass1Parts);
     hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, true>), dim3(nparts), dim3(kThreads), 0, a.stream, ra);
