@@ -39,6 +39,10 @@ def _args():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run 5 device-to-device copies of MIB MiB (a known-size kernel for scaling "
                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--traffic-summary", metavar="DIR", default=None,
+                   help="no GPU: read the rocprofv3 counter CSVs under DIR (pmc_FETCH_SIZE, pmc_WRITE_SIZE "
+                        "of a bench run; cpy_FETCH_SIZE, cpy_WRITE_SIZE of --copy-calibration 1024), write "
+                        "profiles/gemm_fprop8b_traffic.json and exit")
     return p.parse_args()
 
 
@@ -73,8 +77,58 @@ def measured_gemm_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+def _counter_per_dispatch(csv_path, name_part, counter):
+    """Mean over the dispatches of kernels whose name contains name_part of the counter's value
+    summed over all its instances (KiB for FETCH_SIZE / WRITE_SIZE)."""
+    import csv
+    per = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for '{name_part}' in {csv_path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(d):
+    copy_kib = 1024 * 1024  # --copy-calibration 1024: 1 GiB read and 1 GiB written per launch
+    cf, _ = _counter_per_dispatch(os.path.join(d, "cpy_FETCH_SIZE", "p_counter_collection.csv"), "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_per_dispatch(os.path.join(d, "cpy_WRITE_SIZE", "p_counter_collection.csv"), "copyBuffer", "WRITE_SIZE")
+    gf, nf = _counter_per_dispatch(os.path.join(d, "pmc_FETCH_SIZE", "p_counter_collection.csv"), "gemm", "FETCH_SIZE")
+    gw, nw = _counter_per_dispatch(os.path.join(d, "pmc_WRITE_SIZE", "p_counter_collection.csv"), "gemm", "WRITE_SIZE")
+    fs, ws = copy_kib / cf, copy_kib / cw
+    M, N, K = 8192, 14336, 4096
+    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/{d} -o p -- python3 $REPO/bench.py {a}"
+    out = {
+        "what": "HBM-side traffic per launch of the NVFP4 GEMM (fprop 8192x14336x4096, bf16 out), from rocprofv3 "
+                "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the dispatches), each scaled by the "
+                "same counter's reading for a device-to-device copy of 1024 MiB",
+        "commands": [cmd.format(c="FETCH_SIZE", d="pmc_FETCH_SIZE", a="--steps 2 --warmup 1 --no-cpu"),
+                     cmd.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", a="--steps 2 --warmup 1 --no-cpu"),
+                     cmd.format(c="FETCH_SIZE", d="cpy_FETCH_SIZE", a="--copy-calibration 1024"),
+                     cmd.format(c="WRITE_SIZE", d="cpy_WRITE_SIZE", a="--copy-calibration 1024"),
+                     "python3 bench.py --traffic-summary gpurun_out"],
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1), "copy_true_kib_each_way": copy_kib,
+        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+        "gemm_dispatches": [nf, nw],
+        "gemm_fetch_kib_per_launch": round(gf, 1), "gemm_write_kib_per_launch": round(gw, 1),
+        "traffic_bytes_per_launch": int(round((gf * fs + gw * ws) * 1024)),
+        "algorithmic_operand_bytes": M * K // 2 + N * K // 2 + M * K // 16 + N * K // 256,
+        "output_bytes": M * N * 2,
+        "gemm_source_sha256": gemm_source_digest(),
+    }
+    path = os.path.join(ROOT, "profiles", "gemm_fprop8b_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     a = _args()
+    if a.traffic_summary:
+        traffic_summary(a.traffic_summary)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
@@ -148,15 +202,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # per-kernel times: eager launches bracketed by events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    for s in range(a.steps):
-        e = evs[s]
-        e[0].record(); q_a(); e[1].record(); q_b(); e[2].record(); mm(); e[3].record()
+    # per-call times of each library call: `steps` back-to-back launches on the launch stream
+    # bracketed by two events (the library launches on torch's current stream); a GEMM queued first
+    # keeps the GPU busy while the host enqueues them, so host launch overhead is not timed
+    def per_call_ms(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        mm()  # ~0.7 ms of queued GPU work, so that the launches below are enqueued ahead of the GPU
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    qa_ms = per_call_ms(q_a)
+    qb_ms = per_call_ms(q_b)
+    mm_ms = per_call_ms(mm)
+    step()
     torch.cuda.synchronize()
-    qa_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
-    qb_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
-    mm_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
     y_eager = y.clone()
 
     # the step as one HIP graph (every library call is capturable: kernels only, no memsets)
@@ -212,7 +276,7 @@ def main():
             "quantize_algorithmic_bytes": qbytes,
             "gemm_ms": round(mm_ms, 4),
             "gemm_tflops": round(gemm_tflops, 1),
-            "step_timing": "HIP graph replay of quantize(A) + quantize(B) + GEMM; components from eager launches",
+            "step_timing": "HIP graph replay of quantize(A) + quantize(B) + GEMM; components: mean of back-to-back launches of each call",
         },
         "roofline": {
             "kernel": "nvfp4 gemm",
