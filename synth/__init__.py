@@ -124,8 +124,15 @@ def wgrad8b(seed=0, tokens=8192, n_out=14336, n_in=4096):
     return dy, x
 
 
-def moe_experts(seed=0, n_experts=64, k=4096, n=1536):
-    return [student_t((k, n), 4, 0.02, seed, 1000 + e) for e in range(n_experts)]
+def moe_experts(seed=0, n_experts=64, k=4096, n=1536, workers=1):
+    """Expert weights [k x n] bf16, Student-t(4) x 0.02; expert e draws from its own generator, so
+    the result does not depend on `workers` (threads that generate experts concurrently)."""
+    make = lambda e: student_t((k, n), 4, 0.02, seed, 1000 + e)
+    if workers <= 1:
+        return [make(e) for e in range(n_experts)]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(make, range(n_experts)))
 
 
 def moe_tokens(seed=0, n_tokens=16384, k=4096):
