@@ -141,6 +141,18 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int y_dtype, int64_t ldy, 
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc,
                int32_t num_groups, const int64_t *group_row_offsets, void *hip_stream);
 
+/* Transpose of an NVFP4 tensor with 16x16 block scales: out = in^T, i.e. out codes [k x rows]
+ * (out->rows == in->k, out->k == in->rows), out scales the transposed [k/16][rows/16] grid, and the
+ * same tensor scale.  With 2D scaling every 16x16 tile shares one scale, so this equals quantizing
+ * Y^T directly (bit for bit): a weight quantized once for the forward GEMM feeds the backward-data
+ * GEMM, whose contraction runs along the other dimension.  (The recipe scales weights in 2D 16x16
+ * blocks: aissential.tech article, Method; hyper.ai (fr) story.  That one 2D quantization serves
+ * both GEMMs is this library's reading: 16x16 tiles map onto 16x16 tiles under transposition.)
+ * Both descriptors must carry NVFP4_BLOCK2D (else NVFP4_ERR_UNSUPPORTED); rows and k multiples of
+ * 16; data 16-byte aligned; all buffers device memory owned by the caller; in and out must not
+ * overlap.  Runs on hip_stream and returns after the enqueue. */
+int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream);
+
 /* Static, human-readable text for a status code. */
 const char *nvfp4_status_string(int status);
 

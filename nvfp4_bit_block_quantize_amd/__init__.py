@@ -24,7 +24,7 @@ __all__ = [
     "NVFP4_ERR_HIP", "NVFP4_F32", "NVFP4_BF16", "NVFP4_COLWISE", "NVFP4_BLOCK2D", "NVFP4_SR",
     "NVFP4_FOUR_OVER_SIX", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
     "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize",
-    "nvfp4_gemm", "nvfp4_status_string", "empty_like_quantized",
+    "nvfp4_gemm", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
 ]
 
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_HIP = range(6)
@@ -65,6 +65,8 @@ def lib():
         L.nvfp4_dequantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [TP, TP, P, ctypes.c_int, i64, i32, ctypes.POINTER(ctypes.c_int64), P]
         L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_transpose.argtypes = [TP, TP, P]
+        L.nvfp4_transpose.restype = ctypes.c_int
         L.nvfp4_status_string.argtypes = [ctypes.c_int]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -213,4 +215,15 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype: torch.dtype = torch.bf
     st = lib().nvfp4_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(out), _dtype_code(out.dtype), _ld(out), G, offs,
                           _stream_handle(out.device))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def nvfp4_transpose(t: NVFP4Tensor, out: Optional[NVFP4Tensor] = None) -> NVFP4Tensor:
+    """Transpose of a 16x16-block-scaled NVFP4 tensor (see include/nvfp4.h): codes, scale grid and
+    tensor scale of t^T, equal to quantizing the transposed matrix directly."""
+    if out is None:
+        out = empty_like_quantized(t.k, t.rows, NVFP4_BLOCK2D, t.data.device)
+    din, dout = t.descriptor(), out.descriptor()
+    st = lib().nvfp4_transpose(ctypes.byref(din), ctypes.byref(dout), _stream_handle(t.data.device))
+    _check(st, "nvfp4_transpose")
     return out

@@ -192,6 +192,30 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
   return status_of(nvfp4::launch_gemm(g));
 }
 
+int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream) {
+  if (!in || !out) return NVFP4_ERR_NULL;
+  if (!(in->flags & NVFP4_BLOCK2D) || !(out->flags & NVFP4_BLOCK2D)) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t R = in->rows, K = in->k;
+  if (R < 0 || K < 0 || R % 16 != 0 || K % 16 != 0 || out->rows != K || out->k != R) return NVFP4_ERR_SHAPE;
+  if (R * K >= kMaxIndex) return NVFP4_ERR_SHAPE;
+  if (!in->tensor_scale || !out->tensor_scale) return NVFP4_ERR_NULL;
+  if (R > 0 && K > 0) {
+    if (!in->data || !in->scales || !out->data || !out->scales) return NVFP4_ERR_NULL;
+    if (!aligned16(in->data) || !aligned16(out->data)) return NVFP4_ERR_ALIGN;
+  }
+  nvfp4::TransposeLaunch t{};
+  t.in_data = in->data;
+  t.in_scales = in->scales;
+  t.in_ts = in->tensor_scale;
+  t.out_data = out->data;
+  t.out_scales = out->scales;
+  t.out_ts = out->tensor_scale;
+  t.R = R;
+  t.K = K;
+  t.stream = static_cast<hipStream_t>(hip_stream);
+  return status_of(nvfp4::launch_transpose(t));
+}
+
 const char *nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "NVFP4_OK: success";

@@ -56,10 +56,20 @@ struct GemmArgs {
   hipStream_t stream;
 };
 
+struct TransposeLaunch {
+  const uint8_t *in_data, *in_scales;
+  const float *in_ts;
+  uint8_t *out_data, *out_scales;
+  float *out_ts;
+  int64_t R, K;  // input logical shape
+  hipStream_t stream;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_quantize(const QuantArgs &a);
 hipError_t launch_dequantize(const DequantArgs &a);
 hipError_t launch_gemm(const GemmArgs &a);
+hipError_t launch_transpose(const TransposeLaunch &a);
 
 // Host copy of the Philox4x32-10 block function (for the RHT sign word).
 void philox4x32_10_host(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);

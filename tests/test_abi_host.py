@@ -117,3 +117,15 @@ def test_status_strings_and_workspace():
         assert nv.nvfp4_status_string(s).startswith("NVFP4_")
     assert "unknown" in nv.nvfp4_status_string(99)
     assert nv.nvfp4_workspace_size(8192, 4096, 0) >= 4 * 1024
+
+
+def test_transpose_validation():
+    L = nv.lib()
+    t = lambda i, o: L.nvfp4_transpose(ctypes.byref(i) if i else None, ctypes.byref(o) if o else None, None)
+    B2 = nv.NVFP4_BLOCK2D
+    assert t(None, _desc(64, 32, B2)) == nv.NVFP4_ERR_NULL
+    assert t(_desc(32, 64), _desc(64, 32, B2)) == nv.NVFP4_ERR_UNSUPPORTED      # 1D scales do not transpose
+    assert t(_desc(32, 64, B2), _desc(64, 32)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert t(_desc(32, 64, B2), _desc(32, 64, B2)) == nv.NVFP4_ERR_SHAPE        # out must be [k x rows]
+    assert t(_desc(40, 64, B2), _desc(64, 40, B2)) == nv.NVFP4_ERR_SHAPE        # rows % 16
+    assert t(_desc(32, 64, B2, data=MIS), _desc(64, 32, B2)) == nv.NVFP4_ERR_ALIGN
