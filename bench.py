@@ -33,7 +33,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b"])
+    p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b", "dgrad8b"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -160,6 +160,17 @@ def main():
         out_dtype = torch.bfloat16
         workload = "Llama-3-8B FFN fprop: X[8192x4096] bf16 1D blocks, W[14336x4096] bf16 16x16 tiles, Y bf16"
         qbytes = quant_bytes(M, K, False) + quant_bytes(N, K, True)
+    elif a.workload == "dgrad8b":
+        dy_cpu, _ = synth.wgrad8b(0)
+        _, w_cpu = synth.fprop8b(0)
+        x_cpu = dy_cpu  # A = dY (rows, K = 14336, stochastic rounding); B = transpose of Q2D(W)
+        M, K = x_cpu.shape
+        N = w_cpu.shape[1]
+        fa, fb, rht = nv.NVFP4_SR, nv.NVFP4_BLOCK2D, False
+        out_dtype = torch.bfloat16
+        workload = "Llama-3-8B FFN dgrad: dY[8192x14336] SR rows, W[14336x4096] 16x16 tiles transposed, dX bf16"
+        # the B side of a step moves the 2D-quantized W through nvfp4_transpose (codes + scales, both ways)
+        qbytes = quant_bytes(M, K, False) + 2 * (N * K // 2 + N * K // 256)
     else:
         dy_cpu, xx_cpu = synth.wgrad8b(0)
         x_cpu, w_cpu = dy_cpu, xx_cpu  # A = dY^T, B = X^T
@@ -176,6 +187,12 @@ def main():
     R_b, K_b = (w.shape[1], w.shape[0]) if fb & nv.NVFP4_COLWISE else tuple(w.shape)
     qa = nv.empty_like_quantized(R_a, K_a, fa, dev)
     qb = nv.empty_like_quantized(R_b, K_b, fb, dev)
+    qw_fwd = None
+    if a.workload == "dgrad8b":
+        # the forward pass's 2D quantization of W (not part of the dgrad step); the step's B operand
+        # is its transpose [4096 x 14336]
+        qw_fwd = nv.nvfp4_quantize(w, flags=nv.NVFP4_BLOCK2D)
+        qb = nv.empty_like_quantized(w.shape[1], w.shape[0], nv.NVFP4_BLOCK2D, dev)
     ws_a = torch.empty(nv.nvfp4_workspace_size(*x.shape, fa) // 4, dtype=torch.int32, device=dev)
     ws_b = torch.empty(nv.nvfp4_workspace_size(*w.shape, fb) // 4, dtype=torch.int32, device=dev)
     y = torch.empty((M, N), dtype=out_dtype, device=dev)
@@ -184,10 +201,12 @@ def main():
         if rht:
             nv.nvfp4_rht_quantize(x, 7, flags=fa, seed=7, out=qa, workspace=ws_a)
         else:
-            nv.nvfp4_quantize(x, flags=fa, out=qa, workspace=ws_a)
+            nv.nvfp4_quantize(x, flags=fa, seed=7, out=qa, workspace=ws_a)
 
     def q_b():
-        if rht:
+        if qw_fwd is not None:
+            nv.nvfp4_transpose(qw_fwd, out=qb)
+        elif rht:
             nv.nvfp4_rht_quantize(w, 7, flags=fb, out=qb, workspace=ws_b)
         else:
             nv.nvfp4_quantize(w, flags=fb, out=qb, workspace=ws_b)

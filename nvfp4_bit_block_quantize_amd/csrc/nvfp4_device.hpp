@@ -66,25 +66,21 @@ __device__ __forceinline__ uint32_t e2m1_rne_index(float v) {
 }
 
 // Stochastic rounding of v >= 0 with 16 random bits r16: between the grid neighbours lo <= v < hi
-// round up iff r16 < f * 65536, f = (v - lo) / (hi - lo) (exact); v >= 6 gives 6.
+// round up iff r16 < f * 65536, f = (v - lo) / (hi - lo) (exact); v >= 6 gives 6.  Both sub-ranges
+// are evaluated and selected (no divergent branches): below 1 the step is 0.5; from 1 up, lo is v with
+// its mantissa cut to one bit and the step is 2^(e-1) for v in [2^e, 2^(e+1)).
 __device__ __forceinline__ uint32_t e2m1_sr_index(float v, uint32_t r16) {
-  if (v >= 6.0f) return 7u;
-  uint32_t idx;
-  float f16;  // f * 65536, exact
-  if (v < 1.0f) {
-    bool half = v >= 0.5f;
-    float lo = half ? 0.5f : 0.0f;
-    idx = half ? 1u : 0u;
-    f16 = (v - lo) * 131072.0f;  // step 0.5
-  } else {
-    uint32_t b = __float_as_uint(v);
-    float lo = __uint_as_float(b & 0xFFC00000u);  // truncate to one mantissa bit
-    idx = (b >> 22) - 252u;                         // 1 -> 2, 1.5 -> 3, 2 -> 4, ..., 4 -> 6
-    // step = 2^(e-1) for v in [2^e, 2^(e+1)); 65536 / step = 2^(17 - e)
-    float scale = __uint_as_float((271u - (b >> 23)) << 23);
-    f16 = (v - lo) * scale;
-  }
-  return idx + ((static_cast<float>(r16) < f16) ? 1u : 0u);
+  const float vc = fminf(v, 6.0f);
+  const uint32_t b = __float_as_uint(vc);
+  const bool small = vc < 1.0f, half = vc >= 0.5f;
+  const float lo = small ? (half ? 0.5f : 0.0f) : __uint_as_float(b & 0xFFC00000u);
+  // 65536 / step: 2^17 below 1, else 2^(17 - e) (the exponent field 271 - biased e; only used when
+  // vc >= 1, where it lies in [129, 144])
+  const float scale = small ? 131072.0f : __uint_as_float((271u - (b >> 23)) << 23);
+  const uint32_t idx = small ? (half ? 1u : 0u) : (b >> 22) - 252u;  // 1 -> 2, 1.5 -> 3, ..., 4 -> 6
+  const float f16 = (vc - lo) * scale;                                // f * 65536, exact
+  const uint32_t r = idx + ((static_cast<float>(r16) < f16) ? 1u : 0u);
+  return v >= 6.0f ? 7u : r;
 }
 
 // ---- Philox4x32-10 -------------------------------------------------------------------------------
@@ -99,14 +95,15 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    uint32_t p0_hi = __umulhi(0xD2511F53u, c0), p0_lo = 0xD2511F53u * c0;
-    uint32_t p1_hi = __umulhi(0xCD9E8D57u, c2), p1_lo = 0xCD9E8D57u * c2;
-    uint32_t n0 = p1_hi ^ c1 ^ k0;
-    uint32_t n2 = p0_hi ^ c3 ^ k1;
+    // full 64-bit products: one v_mad_u64_u32 each gives both halves
+    const uint64_t p0 = static_cast<uint64_t>(c0) * 0xD2511F53u;
+    const uint64_t p1 = static_cast<uint64_t>(c2) * 0xCD9E8D57u;
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = p1_lo;
+    c1 = static_cast<uint32_t>(p1);
     c2 = n2;
-    c3 = p0_lo;
+    c3 = static_cast<uint32_t>(p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
