@@ -17,6 +17,8 @@ COLWISE = 1
 BLOCK2D = 2
 SR = 4
 FOUR_OVER_SIX = 8
+TS_FOR_FOUR = 16
+SCALE_SEARCH = 32
 
 DT_F32 = 0
 DT_BF16 = 1

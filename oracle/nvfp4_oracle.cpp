@@ -241,12 +241,16 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
   const bool block2d = (flags & OR_BLOCK2D) != 0;
   const bool sr = (flags & OR_SR) != 0;
   const bool fos = (flags & OR_FOUR_OVER_SIX) != 0;
+  const bool search = (flags & OR_SCALE_SEARCH) != 0;
+  const bool ts_four = (flags & OR_TS_FOR_FOUR) != 0;
   if (rows < 0 || cols < 0 || ldx < cols) return 2;
   const int64_t R = colwise ? cols : rows;
   const int64_t K = colwise ? rows : cols;
   if (K % 16 != 0) return 2;
   if (block2d && R % 16 != 0) return 2;
-  if ((sr && fos) || (sr && block2d) || (fos && block2d) || (use_rht && block2d)) return 4;
+  if ((sr && (fos || search)) || (sr && block2d) || (fos && search) || (search && block2d) ||
+      (use_rht && block2d))
+    return 4;
 
   /* Y[r][k] materialised in fp32 (bf16 widened exactly). */
   std::vector<float> Y(static_cast<size_t>(R * K));
@@ -287,7 +291,7 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
   }
   float A = 0.0f;
   for (float m : part) A = std::max(A, m);
-  const float ts = A / 2688.0f;
+  const float ts = ts_four ? A / 1792.0f : A / 2688.0f;
   *ts_out = ts;
 
   QuantCtx c{R, K, flags, seed, stream_id, ts};
@@ -311,6 +315,38 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
             for (int64_t t = 0; t < 16; ++t)
               ab = std::max(ab, std::fabs(Y[static_cast<size_t>(r * K + 16 * kb + t)]));
           uint8_t sb = block_scale_byte(ab, 6.0f, ts);
+          if (fos) {
+            /* Four-over-Six on the tile: the same choice as for a 1D block, with the tile SSE
+             * summed by quadrants (see the header) */
+            auto tile_sse = [&](uint8_t sbx) {
+              float q[2][2];
+              for (int qi = 0; qi < 2; ++qi)
+                for (int qj = 0; qj < 2; ++qj) {
+                  float acc = 0.0f;
+                  for (int64_t r = r0 + 8 * qi; r < r0 + 8 * qi + 8; ++r)
+                    for (int64_t t = 8 * qj; t < 8 * qj + 8; ++t) {
+                      int64_t k = 16 * kb + t;
+                      float y = Y[static_cast<size_t>(r * K + k)];
+                      float diff = y - decode_element(encode_element(c, y, sbx, r, k), sbx, ts);
+                      acc = std::fmaf(diff, diff, acc);
+                    }
+                  q[qi][qj] = acc;
+                }
+              float top = q[0][0] + q[0][1];
+              float bottom = q[1][0] + q[1][1];
+              return top + bottom;
+            };
+            const float acc6 = tile_sse(sb);
+            const uint8_t sb4 = block_scale_byte(ab, 4.0f, ts);
+            const float acc4 = tile_sse(sb4);
+            sse_plain[static_cast<size_t>(r0)] += acc6;
+            if (acc4 < acc6) {
+              sb = sb4;
+              sse_chosen[static_cast<size_t>(r0)] += acc4;
+            } else {
+              sse_chosen[static_cast<size_t>(r0)] += acc6;
+            }
+          }
           scales[(r0 / 16) * KB + kb] = sb;
           for (int64_t r = r0; r < r0 + 16; ++r)
             for (int64_t t = 0; t < 16; ++t) {
@@ -330,30 +366,35 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
           uint8_t codes[16];
           uint8_t sb = block_scale_byte(ab, 6.0f, ts);
           for (int t = 0; t < 16; ++t) codes[t] = encode_element(c, y[t], sb, r, 16 * kb + t);
-          if (fos) {
-            /* Four-over-Six: also try mapping the block max to 4; keep the lower block SSE
-             * (fp32, fused multiply-add in block order); a tie keeps 6. ts is unchanged. */
-            float acc6 = 0.0f;
-            for (int t = 0; t < 16; ++t) {
-              float diff = y[t] - decode_element(codes[t], sb, ts);
-              acc6 = std::fmaf(diff, diff, acc6);
+          if (fos || search) {
+            /* Four-over-Six (targets 6, 4) or the scale search (6, 5.5, 5, 4.5, 4): each target
+             * gives a block scale and codes; keep the one with the lowest block SSE (fp32, fused
+             * multiply-add in block order); a later target must be strictly lower.  ts is
+             * unchanged. */
+            static const float kFos[] = {6.0f, 4.0f};
+            static const float kSearch[] = {6.0f, 5.5f, 5.0f, 4.5f, 4.0f};
+            const float *targets = search ? kSearch : kFos;
+            const int nt = search ? 5 : 2;
+            float best = 0.0f;
+            for (int ti = 0; ti < nt; ++ti) {
+              const uint8_t sbx = ti == 0 ? sb : block_scale_byte(ab, targets[ti], ts);
+              uint8_t cx[16];
+              float acc = 0.0f;
+              for (int t = 0; t < 16; ++t) {
+                cx[t] = ti == 0 ? codes[t] : encode_element(c, y[t], sbx, r, 16 * kb + t);
+                float diff = y[t] - decode_element(cx[t], sbx, ts);
+                acc = std::fmaf(diff, diff, acc);
+              }
+              if (ti == 0) {
+                best = acc;
+                sse_plain[static_cast<size_t>(r)] += acc;
+              } else if (acc < best) {
+                best = acc;
+                sb = sbx;
+                std::memcpy(codes, cx, 16);
+              }
             }
-            uint8_t sb4 = block_scale_byte(ab, 4.0f, ts);
-            uint8_t codes4[16];
-            float acc4 = 0.0f;
-            for (int t = 0; t < 16; ++t) {
-              codes4[t] = encode_element(c, y[t], sb4, r, 16 * kb + t);
-              float diff = y[t] - decode_element(codes4[t], sb4, ts);
-              acc4 = std::fmaf(diff, diff, acc4);
-            }
-            sse_plain[static_cast<size_t>(r)] += acc6;
-            if (acc4 < acc6) {
-              sb = sb4;
-              std::memcpy(codes, codes4, 16);
-              sse_chosen[static_cast<size_t>(r)] += acc4;
-            } else {
-              sse_chosen[static_cast<size_t>(r)] += acc6;
-            }
+            sse_chosen[static_cast<size_t>(r)] += best;
           }
           scales[r * KB + kb] = sb;
           for (int t = 0; t < 16; ++t) store_code(r, 16 * kb + t, codes[t]);

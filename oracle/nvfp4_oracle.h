@@ -40,7 +40,9 @@ extern "C" {
 #define OR_COLWISE       1u  /* logical Y = x^T: blocks run along x's dim 0            */
 #define OR_BLOCK2D       2u  /* one scale per 16x16 tile of Y                            */
 #define OR_SR            4u  /* stochastic rounding of elements (Philox4x32-10)          */
-#define OR_FOUR_OVER_SIX 8u  /* per block, target 6 or 4 by lower block SSE              */
+#define OR_FOUR_OVER_SIX 8u  /* per block (1D) or 16x16 tile (2D), target 6 or 4 by lower SSE */
+#define OR_TS_FOR_FOUR  16u  /* tensor scale amax / (4*448): a block scale for target 4 never clamps */
+#define OR_SCALE_SEARCH 32u  /* per 1D block, target in {6, 5.5, 5, 4.5, 4} by lowest block SSE */
 
 #define OR_DT_F32  0
 #define OR_DT_BF16 1
@@ -67,10 +69,14 @@ void or_rht16_array(float *u, int64_t nchunks, uint32_t sign_word); /* or_rht16 
  * COLWISE R=cols, K=rows.  Outputs (caller-allocated host buffers):
  *   data   [R][K/2]   packed codes, low nibble = even k
  *   scales [R][K/16]  (1D) or [R/16][K/16] (BLOCK2D), E4M3 bytes
- *   ts     1 float    tensor scale = amax / 2688
+ *   ts     1 float    tensor scale = amax / 2688 (amax / 1792 with OR_TS_FOR_FOUR)
  *   rht_out (nullable, only with use_rht) [R][K] fp32 transformed Y
  *   sse2   (nullable) [0] = sum of chosen block SSE, [1] = sum of plain (target 6) block SSE;
- *          filled for FOUR_OVER_SIX only
+ *          filled for FOUR_OVER_SIX and SCALE_SEARCH only
+ * Block SSE: fp32, diff = RN(y - xhat), acc = fma(diff, diff, acc) in block order (1D); for a
+ * 16x16 tile the four 8x8 quadrants are summed so in row-major order each and combined as
+ * RN(RN(S00 + S01) + RN(S10 + S11)) (S_ij: rows 8i.., columns 8j..).  A candidate replaces the
+ * current choice only if its SSE is strictly lower (candidates in the order listed above).
  * Returns 0 on success, nonzero on an unsupported shape / mode.                                */
 int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
                 uint64_t seed, uint32_t stream_id, int use_rht, uint64_t sign_seed,
