@@ -68,8 +68,17 @@ enum {
   NVFP4_SR = 1u << 2,
   /* Four-over-Six (hyper.ai (de) story on the Nemotron 3 Ultra NVFP4 checkpoint): per 1D block,
    * map the block maximum to 6 or to 4, whichever gives the lower block squared error (fp32,
-   * fused multiply-add in block order; a tie keeps 6).  ts is unchanged. */
-  NVFP4_FOUR_OVER_SIX = 1u << 3
+   * fused multiply-add in block order; a tie keeps 6).  ts is unchanged.  With NVFP4_BLOCK2D the
+   * choice is made per 16x16 tile, its squared error summed per 8x8 quadrant in row-major order and
+   * combined as (top-left + top-right) + (bottom-left + bottom-right). */
+  NVFP4_FOUR_OVER_SIX = 1u << 3,
+  /* Tensor scale amax / (4 * 448) instead of amax / (6 * 448): a block scale for target 4 then
+   * never clamps at the E4M3 maximum (a variant of Four-over-Six; combinable with every mode). */
+  NVFP4_TS_FOR_FOUR = 1u << 4,
+  /* Scale search (an ablation of Four-over-Six): per 1D block, the lowest squared error among the
+   * targets 6, 5.5, 5, 4.5, 4 (tried in that order; a later target must be strictly better).  Not
+   * with NVFP4_SR, NVFP4_FOUR_OVER_SIX or NVFP4_BLOCK2D. */
+  NVFP4_SCALE_SEARCH = 1u << 5
 };
 
 /* Non-owning view of one NVFP4 tensor: logical matrix [rows x k], k contiguous (the contraction

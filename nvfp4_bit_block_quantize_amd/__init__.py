@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_UNSUPPORTED",
     "NVFP4_ERR_HIP", "NVFP4_F32", "NVFP4_BF16", "NVFP4_COLWISE", "NVFP4_BLOCK2D", "NVFP4_SR",
-    "NVFP4_FOUR_OVER_SIX", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
+    "NVFP4_FOUR_OVER_SIX", "NVFP4_TS_FOR_FOUR", "NVFP4_SCALE_SEARCH", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
     "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize",
     "nvfp4_gemm", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
 ]
@@ -30,6 +30,7 @@ __all__ = [
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_HIP = range(6)
 NVFP4_F32, NVFP4_BF16 = 0, 1
 NVFP4_COLWISE, NVFP4_BLOCK2D, NVFP4_SR, NVFP4_FOUR_OVER_SIX = 1, 2, 4, 8
+NVFP4_TS_FOR_FOUR, NVFP4_SCALE_SEARCH = 16, 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

@@ -9,7 +9,8 @@
 
 namespace {
 
-constexpr uint32_t kKnownFlags = NVFP4_COLWISE | NVFP4_BLOCK2D | NVFP4_SR | NVFP4_FOUR_OVER_SIX;
+constexpr uint32_t kKnownFlags =
+    NVFP4_COLWISE | NVFP4_BLOCK2D | NVFP4_SR | NVFP4_FOUR_OVER_SIX | NVFP4_TS_FOR_FOUR | NVFP4_SCALE_SEARCH;
 constexpr int64_t kMaxIndex = int64_t(1) << 32;  // element / chunk counts are 32-bit in the kernels
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -19,7 +20,9 @@ int dtype_size(int dt) { return dt == NVFP4_F32 ? 4 : (dt == NVFP4_BF16 ? 2 : 0)
 int check_flags(uint32_t flags, bool rht) {
   if (flags & ~kKnownFlags) return NVFP4_ERR_UNSUPPORTED;
   const bool sr = flags & NVFP4_SR, fos = flags & NVFP4_FOUR_OVER_SIX, b2d = flags & NVFP4_BLOCK2D;
-  if ((sr && fos) || (sr && b2d) || (fos && b2d) || (rht && b2d)) return NVFP4_ERR_UNSUPPORTED;
+  const bool search = flags & NVFP4_SCALE_SEARCH;
+  if ((sr && (fos || search)) || (sr && b2d) || (fos && search) || (search && b2d) || (rht && b2d))
+    return NVFP4_ERR_UNSUPPORTED;
   return NVFP4_OK;
 }
 

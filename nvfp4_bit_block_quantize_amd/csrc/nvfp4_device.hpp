@@ -11,7 +11,7 @@
 
 namespace nvfp4 {
 
-enum Mode : int { kRNE = 0, kSR = 1, kFourOverSix = 2 };
+enum Mode : int { kRNE = 0, kSR = 1, kFourOverSix = 2, kSearch = 3 };
 
 // ---- bf16 / f32 unpacking --------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -171,7 +171,9 @@ __device__ __forceinline__ float block_sse(const float (&y)[16], uint32_t w0, ui
   return acc;
 }
 
-// Full encode of one 1D block: scale byte and two packed words (nibble t at bits 4t).
+// Full encode of one 1D block: scale byte and two packed words (nibble t at bits 4t).  With
+// Four-over-Six (targets 6, 4) or the scale search (6, 5.5, 5, 4.5, 4) every target gives a scale
+// and codes; the block keeps the lowest squared error, a later target only if strictly lower.
 template <int MODE>
 __device__ __forceinline__ void encode_block(const float (&y)[16], float ab, float ts, uint64_t i0, uint32_t key0,
                                              uint32_t key1, uint32_t stream_id, uint32_t &sbyte, uint32_t &w0,
@@ -179,18 +181,23 @@ __device__ __forceinline__ void encode_block(const float (&y)[16], float ab, flo
   float S;
   sbyte = block_scale(ab, 6.0f, ts, S);
   block_words<MODE>(y, encode_factor(S, ts), i0, key0, key1, stream_id, w0, w1);
-  if constexpr (MODE == kFourOverSix) {
-    // Four-over-Six: also map the block maximum to 4; keep it only if the block SSE is lower
-    const float acc6 = block_sse(y, w0, w1, S, ts);
-    float S4;
-    const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
-    uint32_t v0, v1;
-    block_words<kRNE>(y, encode_factor(S4, ts), i0, key0, key1, stream_id, v0, v1);
-    const float acc4 = block_sse(y, v0, v1, S4, ts);
-    if (acc4 < acc6) {
-      sbyte = sb4;
-      w0 = v0;
-      w1 = v1;
+  if constexpr (MODE == kFourOverSix || MODE == kSearch) {
+    constexpr int NT = MODE == kSearch ? 5 : 2;
+    float best = block_sse(y, w0, w1, S, ts);
+#pragma unroll
+    for (int ti = 1; ti < NT; ++ti) {
+      const float T = MODE == kSearch ? 6.0f - 0.5f * ti : 4.0f;  // 5.5, 5, 4.5, 4 (exact)
+      float Sx;
+      const uint32_t sbx = block_scale(ab, T, ts, Sx);
+      uint32_t v0, v1;
+      block_words<kRNE>(y, encode_factor(Sx, ts), i0, key0, key1, stream_id, v0, v1);
+      const float acc = block_sse(y, v0, v1, Sx, ts);
+      if (acc < best) {
+        best = acc;
+        sbyte = sbx;
+        w0 = v0;
+        w1 = v1;
+      }
     }
   }
 }
@@ -219,15 +226,15 @@ __device__ __forceinline__ void write_partial(uint32_t m, uint32_t *__restrict__
 
 // Tensor amax from the pass-1 partial maxima (float bits of non-negative values compare like
 // unsigned integers), reduced by every wave on its own (at most kPass1Parts values, no barrier);
-// ts = amax / 2688; wave 0 of workgroup 0 publishes ts.
+// ts = amax / ts_div; wave 0 of workgroup 0 publishes ts.
 __device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ partial, uint32_t nparts,
-                                              float *__restrict__ ts_out) {
+                                              float *__restrict__ ts_out, float ts_div) {
   const uint32_t lane = threadIdx.x & 63u;
   uint32_t m = 0;
 #pragma unroll 4
   for (uint32_t i = lane; i < nparts; i += 64) m = max(m, partial[i]);
   m = wave_max_u32(m);
-  const float ts = __uint_as_float(m) / 2688.0f;
+  const float ts = __uint_as_float(m) / ts_div;  // 2688 (6 * 448), or 1792 (4 * 448)
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
   return ts;
 }
@@ -293,6 +300,7 @@ struct RowArgs {
   float *ts_out;
   uint32_t key0, key1, stream_id, sign_word;
   float *rht_out;
+  float ts_div;
 };
 
 template <int ESZ, int MODE, bool RHT, bool PASS1>
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   Raw16<ESZ> cur, nxt;
   if (b < p.nblocks) cur = load_raw16<ESZ>(src(b));
   float ts = 0.0f;
-  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out);
+  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
   uint32_t mx = 0;
   while (b < p.nblocks) {
     const uint32_t bn = b + stride;
@@ -337,6 +345,28 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   if constexpr (PASS1) write_partial(mx, p.partial_out);
 }
 
+// Nearest-even codes of 8 values under factor e (e = +inf: S * ts underflowed, see code_degenerate).
+__device__ __forceinline__ uint32_t codes8(const float (&yv)[8], float e) {
+  if (__builtin_isinf(e)) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w |= code_degenerate(yv[c]) << (4 * c);
+    return w;
+  }
+  return pack8_rne(yv, e);
+}
+
+// fp32 squared error of 8 values against their codes w under scale S, accumulated into acc with fma
+// in order.
+__device__ __forceinline__ float sse8(const float (&yv)[8], uint32_t w, float S, float ts, float acc) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float diff = yv[c] - decode((w >> (4 * c)) & 15u, S, ts);
+    acc = fmaf(diff, diff, acc);
+  }
+  return acc;
+}
+
 // ---- ROW mode, 16x16 tiles --------------------------------------------------------------------------
 struct Row2dArgs {
   const uint8_t *x;
@@ -349,6 +379,7 @@ struct Row2dArgs {
   uint8_t *data;
   uint8_t *scales;
   float *ts_out;
+  float ts_div;
 };
 
 template <int ESZ>
@@ -365,7 +396,27 @@ __device__ __forceinline__ void load_patch(Raw8<ESZ> (&v)[16], const uint8_t *__
   }
 }
 
+// Four-over-Six tile error for the lane pair of a 16x16 tile (even lane: columns 0-7, odd lane:
+// columns 8-15, each 16 rows): quadrant sums in row-major order, (TL + TR) + (BL + BR).
 template <int ESZ>
+__device__ __forceinline__ float tile_sse_rows(const Raw8<ESZ> (&v)[16], float e, float S, float ts) {
+  float top = 0.0f, bottom = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    float yv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) yv[c] = raw8_elem<ESZ>(v[t], c);
+    const uint32_t w = codes8(yv, e);
+    if (t < 8)
+      top = sse8(yv, w, S, ts, top);
+    else
+      bottom = sse8(yv, w, S, ts, bottom);
+  }
+  const float top_o = __shfl_xor(top, 1, 64), bottom_o = __shfl_xor(bottom, 1, 64);
+  return (top + top_o) + (bottom + bottom_o);
+}
+
+template <int ESZ, bool FOS>
 __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
@@ -382,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
     start(task, r0, c0);
     load_patch<ESZ>(v, p.x + r0 * p.ldx_bytes + c0 * ESZ, p.ldx_bytes, c0 < p.K);
   }
-  const float ts = tensor_scale(p.partial, p.nparts, p.ts_out);
+  const float ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
   while (task < p.ntasks) {
     const bool valid = c0 < p.K;  // K % 16 == 0: both lanes of a tile agree
     float ab = 0.0f;
@@ -392,21 +443,27 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
       for (int c = 0; c < 8; ++c) ab = fmaxf(ab, fabsf(raw8_elem<ESZ>(v[t], c)));
     ab = fmaxf(ab, __shfl_xor(ab, 1, 64));
     float S;
-    const uint32_t sb = block_scale(ab, 6.0f, ts, S);
-    const float e = encode_factor(S, ts);
+    uint32_t sb = block_scale(ab, 6.0f, ts, S);
+    float e = encode_factor(S, ts);
+    if constexpr (FOS) {
+      // Four-over-Six on the tile: target 4 only if its tile error is strictly lower
+      const float sse6 = tile_sse_rows<ESZ>(v, e, S, ts);
+      float S4;
+      const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
+      const float e4 = encode_factor(S4, ts);
+      const float sse4 = tile_sse_rows<ESZ>(v, e4, S4, ts);
+      if (sse4 < sse6) {
+        sb = sb4;
+        e = e4;
+      }
+    }
     uint32_t w[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       float yv[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) yv[c] = raw8_elem<ESZ>(v[t], c);
-      if (__builtin_isinf(e)) {
-        w[t] = 0u;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) w[t] |= code_degenerate(yv[c]) << (4 * c);
-      } else {
-        w[t] = pack8_rne(yv, e);
-      }
+      w[t] = codes8(yv, e);
     }
     const int64_t wr0 = r0, wc0 = c0;
     // next task's loads go out before this task's stores
@@ -439,6 +496,7 @@ struct ColArgs {
   float *ts_out;
   uint32_t key0, key1, stream_id, sign_word;
   float *rht_out;
+  float ts_div;
 };
 
 constexpr int kColTokens = 256;  // per workgroup tile
@@ -469,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
   }
   float ts = 0.0f;
-  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out);
+  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
   for (; tile < p.ntiles; tile += gridDim.x) {
     if constexpr (PASS1) {
 #pragma unroll
@@ -497,6 +555,36 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       ab = fmaxf(ab, __shfl_xor(ab, 1, 64));
       sb2d = block_scale(ab, 6.0f, ts, S2d);
       e2d = encode_factor(S2d, ts);
+      if constexpr (MODE == kFourOverSix) {
+        // Four-over-Six on the tile: this lane holds 8 rows (top or bottom half of the tile) of all
+        // 16 columns; quadrant sums in row-major order, (TL + TR) + (BL + BR)
+        auto tile_sse = [&](float e, float S) {
+          float left = 0.0f, right = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float a[8], b[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              a[t] = raw8_elem<ESZ>(v[t], c);
+              b[t] = raw8_elem<ESZ>(v[8 + t], c);
+            }
+            left = sse8(a, codes8(a, e), S, ts, left);
+            right = sse8(b, codes8(b, e), S, ts, right);
+          }
+          const float half = left + right;
+          return half + __shfl_xor(half, 1, 64);
+        };
+        const float sse6 = tile_sse(e2d, S2d);
+        float S4;
+        const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
+        const float e4 = encode_factor(S4, ts);
+        const float sse4 = tile_sse(e4, S4);
+        if (sse4 < sse6) {
+          sb2d = sb4;
+          S2d = S4;
+          e2d = e4;
+        }
+      }
       if (valid && (tj & 1u) == 0) p.scales[(rr / 16) * KB + kk / 16] = static_cast<uint8_t>(sb2d);
     }
 #pragma unroll
@@ -589,7 +677,9 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   const bool b2d = (a.flags & 2u) != 0;
   const bool sr = (a.flags & 4u) != 0;
   const bool fos = (a.flags & 8u) != 0;
-  const int mode = sr ? kSR : (fos ? kFourOverSix : kRNE);
+  const bool search = (a.flags & 32u) != 0;
+  const float ts_div = (a.flags & 16u) != 0 ? 1792.0f : 2688.0f;  // amax / (4 * 448) or / (6 * 448)
+  const int mode = sr ? kSR : (fos ? kFourOverSix : (search ? kSearch : kRNE));
   const int64_t ldx_bytes = a.ldx * ESZ;
   const uint32_t key0 = static_cast<uint32_t>(a.seed), key1 = static_cast<uint32_t>(a.seed >> 32);
   const uint8_t *x = static_cast<const uint8_t *>(a.x);
@@ -601,13 +691,14 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   uint32_t col_tiles = 0;
   if (!colwise) {
     ra = RowArgs{x, ldx_bytes, static_cast<uint32_t>(a.R * (a.K / 16)), make_fastdiv(static_cast<uint32_t>(a.K / 16)), a.K,
-                 a.workspace, 0, a.workspace, a.data, a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out};
+                 a.workspace, 0, a.workspace, a.data, a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out,
+                 ts_div};
   } else {
     const uint32_t ntr = static_cast<uint32_t>((a.R + kColCols - 1) / kColCols);
     const uint32_t ntk = static_cast<uint32_t>((a.K + kColTokens - 1) / kColTokens);
     col_tiles = ntr * ntk;
     ca = ColArgs{x, ldx_bytes, a.K, a.R, col_tiles, make_fastdiv(ntr), a.workspace, 0, a.workspace, a.data,
-                 a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out};
+                 a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out, ts_div};
   }
 
   // ---- pass 1
@@ -634,27 +725,36 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     ra.nparts = nparts;
     const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, kPass2Grid);
     const dim3 g(grid), blk(kThreads);
+#define NVFP4_ROW(MODE_, RHT_) hipLaunchKernelGGL((row1d_kernel<ESZ, MODE_, RHT_, false>), g, blk, 0, a.stream, ra)
     if (a.rht) {
       if (mode == kSR)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, true, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kSR, true);
       else if (mode == kFourOverSix)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, true, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kFourOverSix, true);
+      else if (mode == kSearch)
+        NVFP4_ROW(kSearch, true);
       else
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kRNE, true);
     } else {
       if (mode == kSR)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kSR, false, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kSR, false);
       else if (mode == kFourOverSix)
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kFourOverSix, false, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kFourOverSix, false);
+      else if (mode == kSearch)
+        NVFP4_ROW(kSearch, false);
       else
-        hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, false, false>), g, blk, 0, a.stream, ra);
+        NVFP4_ROW(kRNE, false);
     }
+#undef NVFP4_ROW
   } else if (!colwise && b2d) {
     const uint32_t nseg = static_cast<uint32_t>((a.K + 511) / 512);
     Row2dArgs r2{x, ldx_bytes, static_cast<uint32_t>((a.R / 16) * nseg), make_fastdiv(nseg), a.K, a.workspace, nparts,
-                 a.data, a.scales, a.ts};
+                 a.data, a.scales, a.ts, ts_div};
     const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid);
-    hipLaunchKernelGGL(row2d_kernel<ESZ>, dim3(grid), dim3(kThreads), 0, a.stream, r2);
+    if (fos)
+      hipLaunchKernelGGL((row2d_kernel<ESZ, true>), dim3(grid), dim3(kThreads), 0, a.stream, r2);
+    else
+      hipLaunchKernelGGL((row2d_kernel<ESZ, false>), dim3(grid), dim3(kThreads), 0, a.stream, r2);
   } else {
     ca.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
@@ -666,8 +766,14 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     else                                                                                                   \
       hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, false>), grid, block, 0, a.stream, ca); \
   } while (0)
-    if (b2d)
+    if (b2d && fos)
+      NVFP4_COL(kFourOverSix, false, true);
+    else if (b2d)
       NVFP4_COL(kRNE, false, true);
+    else if (a.rht && mode == kSearch)
+      NVFP4_COL(kSearch, true, false);
+    else if (mode == kSearch)
+      NVFP4_COL(kSearch, false, false);
     else if (a.rht && mode == kSR)
       NVFP4_COL(kSR, true, false);
     else if (a.rht && mode == kFourOverSix)

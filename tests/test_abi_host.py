@@ -68,7 +68,10 @@ def test_quantize_validation(rht):
     assert _q(flags=1 << 7, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
     assert _q(flags=nv.NVFP4_SR | nv.NVFP4_FOUR_OVER_SIX, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
     assert _q(flags=nv.NVFP4_SR | nv.NVFP4_BLOCK2D, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
-    assert _q(flags=nv.NVFP4_FOUR_OVER_SIX | nv.NVFP4_BLOCK2D, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_SCALE_SEARCH | nv.NVFP4_BLOCK2D, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_SCALE_SEARCH | nv.NVFP4_FOUR_OVER_SIX, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=nv.NVFP4_SCALE_SEARCH | nv.NVFP4_SR, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(flags=1 << 6, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
 
 
 def test_rht_rejects_2d_and_block2d_rows():
