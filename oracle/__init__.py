@@ -72,6 +72,8 @@ def lib():
         L.or_gemm_ref.argtypes = [P, P, ctypes.c_float, u32, P, P, ctypes.c_float, u32,
                                   i64, i64, i64, P, i64, P, P, ctypes.c_int]
         L.or_gemm_ref.restype = ctypes.c_int
+        L.or_gemm_w4a16_ref.argtypes = [P, i64, P, P, ctypes.c_float, u32, i64, i64, i64, P, i64, P, P, ctypes.c_int]
+        L.or_gemm_w4a16_ref.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -197,4 +199,24 @@ def gemm_ref(a, b, M, N, K, tiles=None, nthreads=None):
                            M, N, K, _p(t), t.shape[0], _p(c), _p(bnd), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle gemm rejected the arguments")
+    return c, bnd
+
+
+def gemm_w4a16_ref(a_bf16_bits, b, M, N, K, tiles=None, nthreads=None):
+    """A: uint16 bf16 bits [M x lda]; b: dict with data/scales/ts/flags (B is N x K).  Returns
+    (C, bound) as float64 [M x N] (NaN outside the requested tiles)."""
+    if tiles is None:
+        tiles = [(0, 0, M, N)]
+    t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int64).reshape(-1, 4))
+    a = np.asarray(a_bf16_bits, dtype=np.uint16)
+    assert a.ndim == 2 and a.strides[1] == 2
+    c = np.full((M, N), np.nan, dtype=np.float64)
+    bnd = np.full((M, N), np.nan, dtype=np.float64)
+    bd = np.ascontiguousarray(b["data"], dtype=np.uint8)
+    bsc = np.ascontiguousarray(b["scales"], dtype=np.uint8)
+    rc = lib().or_gemm_w4a16_ref(_p(a), a.strides[0] // 2, _p(bd), _p(bsc), float(b["ts"]),
+                                 int(b.get("flags", 0)) & BLOCK2D, M, N, K, _p(t), t.shape[0], _p(c), _p(bnd),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle w4a16 gemm rejected the arguments")
     return c, bnd

@@ -475,4 +475,50 @@ int or_gemm_ref(const uint8_t *a_data, const uint8_t *a_scales, float a_ts, uint
   return 0;
 }
 
+int or_gemm_w4a16_ref(const uint16_t *a_bf16, int64_t lda, const uint8_t *b_data, const uint8_t *b_scales,
+                      float b_ts, uint32_t b_flags, int64_t M, int64_t N, int64_t K, const int64_t *tiles,
+                      int64_t n_tiles, double *c, double *bound, int nthreads) {
+  /* C = A * B_hat^T with A bf16 (widened exactly) and B_hat the exact NVFP4 decode: every product
+   * a * (q * S) is exact in binary64, the K sum rounds at 2^-53, ts_b is applied at the end. */
+  if (K % 16 != 0 || lda < K) return 2;
+  const int64_t KB = K / 16;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    int64_t r0 = tiles[4 * t], c0 = tiles[4 * t + 1], h = tiles[4 * t + 2], w = tiles[4 * t + 3];
+    if (r0 < 0 || c0 < 0 || h < 0 || w < 0 || r0 + h > M || c0 + w > N) return 2;
+  }
+  const double tsb = static_cast<double>(b_ts);
+  parallel_ranges(n_tiles, 1, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t) {
+      int64_t r0 = tiles[4 * t], c0 = tiles[4 * t + 1], h = tiles[4 * t + 2], w = tiles[4 * t + 3];
+      std::vector<double> Ad(static_cast<size_t>(h * K)), Bd(static_cast<size_t>(w * K));
+      for (int64_t i = 0; i < h; ++i)
+        for (int64_t k = 0; k < K; ++k)
+          Ad[static_cast<size_t>(i * K + k)] = static_cast<double>(widen_bf16(a_bf16[(r0 + i) * lda + k]));
+      for (int64_t j = 0; j < w; ++j)
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t row = c0 + j;
+          uint8_t byte = b_data[row * (K / 2) + k / 2];
+          uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+          uint8_t sb = (b_flags & OR_BLOCK2D) ? b_scales[(row / 16) * KB + k / 16] : b_scales[row * KB + k / 16];
+          Bd[static_cast<size_t>(j * K + k)] =
+              static_cast<double>(or_e2m1_value(code)) * static_cast<double>(or_e4m3_value(sb));
+        }
+      for (int64_t i = 0; i < h; ++i) {
+        for (int64_t j = 0; j < w; ++j) {
+          double acc = 0.0, bnd = 0.0;
+          const double *ar = &Ad[static_cast<size_t>(i * K)];
+          const double *br = &Bd[static_cast<size_t>(j * K)];
+          for (int64_t k = 0; k < K; ++k) {
+            acc += ar[k] * br[k];
+            bnd += std::fabs(ar[k]) * std::fabs(br[k]);
+          }
+          c[(r0 + i) * N + (c0 + j)] = acc * tsb;
+          bound[(r0 + i) * N + (c0 + j)] = bnd * std::fabs(tsb);
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 } /* extern "C" */

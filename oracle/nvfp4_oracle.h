@@ -98,6 +98,13 @@ int or_gemm_ref(const uint8_t *a_data, const uint8_t *a_scales, float a_ts, uint
                 int64_t M, int64_t N, int64_t K, const int64_t *tiles, int64_t n_tiles,
                 double *c, double *bound, int nthreads);
 
+/* W4A16 reference: C[i][j] = ts_b * sum_k a[i][k] * (q_b S_b)[j][k] in binary64, A given as bf16
+ * bits [M][lda] (widened exactly), B an NVFP4 [N x K] operand (1D or BLOCK2D).  bound as above.
+ * Tiles as for or_gemm_ref. */
+int or_gemm_w4a16_ref(const uint16_t *a_bf16, int64_t lda, const uint8_t *b_data, const uint8_t *b_scales,
+                      float b_ts, uint32_t b_flags, int64_t M, int64_t N, int64_t K, const int64_t *tiles,
+                      int64_t n_tiles, double *c, double *bound, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
