@@ -33,7 +33,9 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="fprop8b", choices=["fprop8b", "wgrad8b", "dgrad8b"])
+    p.add_argument("--workload", default="fprop8b",
+                   choices=["fprop8b", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode"])
+    p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -171,6 +173,19 @@ def main():
         workload = "Llama-3-8B FFN dgrad: dY[8192x14336] SR rows, W[14336x4096] 16x16 tiles transposed, dX bf16"
         # the B side of a step moves the 2D-quantized W through nvfp4_transpose (codes + scales, both ways)
         qbytes = quant_bytes(M, K, False) + 2 * (N * K // 2 + N * K // 256)
+    elif a.workload in ("w4a16_8b", "w4a16_decode"):
+        # weight-only 4-bit: bf16 activations against the 16x16-tile NVFP4 weight, which a serving
+        # stack quantizes once (outside the step); the step is the GEMM alone
+        x_cpu, w_cpu = synth.fprop8b(0)
+        if a.workload == "w4a16_decode":
+            x_cpu = x_cpu[:a.decode_tokens].contiguous()
+        M, K = x_cpu.shape
+        N = w_cpu.shape[0]
+        fa, fb, rht = 0, nv.NVFP4_BLOCK2D, False
+        out_dtype = torch.bfloat16
+        workload = (f"Llama-3-8B FFN fprop, W4A16: X[{M}x4096] bf16 (not quantized), W[14336x4096] NVFP4 "
+                    "16x16 tiles (quantized once, outside the step), Y bf16")
+        qbytes = 0
     else:
         dy_cpu, xx_cpu = synth.wgrad8b(0)
         x_cpu, w_cpu = dy_cpu, xx_cpu  # A = dY^T, B = X^T
@@ -197,13 +212,21 @@ def main():
     ws_b = torch.empty(nv.nvfp4_workspace_size(*w.shape, fb) // 4, dtype=torch.int32, device=dev)
     y = torch.empty((M, N), dtype=out_dtype, device=dev)
 
+    w4a16 = a.workload.startswith("w4a16")
+    if w4a16:
+        qb = nv.nvfp4_quantize(w, flags=fb, workspace=ws_b)
+
     def q_a():
+        if w4a16:
+            return
         if rht:
             nv.nvfp4_rht_quantize(x, 7, flags=fa, seed=7, out=qa, workspace=ws_a)
         else:
             nv.nvfp4_quantize(x, flags=fa, seed=7, out=qa, workspace=ws_a)
 
     def q_b():
+        if w4a16:
+            return
         if qw_fwd is not None:
             nv.nvfp4_transpose(qw_fwd, out=qb)
         elif rht:
@@ -212,7 +235,10 @@ def main():
             nv.nvfp4_quantize(w, flags=fb, out=qb, workspace=ws_b)
 
     def mm():
-        nv.nvfp4_gemm(qa, qb, out=y)
+        if w4a16:
+            nv.nvfp4_gemm_w4a16(x, qb, out=y)
+        else:
+            nv.nvfp4_gemm(qa, qb, out=y)
 
     def step():
         q_a(); q_b(); mm()
@@ -235,8 +261,8 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) / a.steps
 
-    qa_ms = per_call_ms(q_a)
-    qb_ms = per_call_ms(q_b)
+    qa_ms = per_call_ms(q_a) if not w4a16 else 0.0
+    qb_ms = per_call_ms(q_b) if not w4a16 else 0.0
     mm_ms = per_call_ms(mm)
     step()
     torch.cuda.synchronize()
@@ -270,7 +296,9 @@ def main():
     ms_step = wall * 1e3 / a.steps
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (mm_ms * 1e-3) / 1e12
-    quant_gbps = qbytes / ((qa_ms + qb_ms) * 1e-3) / 1e9
+    quant_gbps = qbytes / ((qa_ms + qb_ms) * 1e-3) / 1e9 if qbytes else 0.0
+    # HBM bytes a W4A16 GEMM must move at least once: bf16 A, the weight's codes and scales, C
+    w4_bytes = M * K * 2 + N * K // 2 + N * K // 256 + M * N * 2
     value = flops / (ms_step * 1e-3) / 1e12
 
     result = {
@@ -304,10 +332,21 @@ def main():
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
-            "traffic": measured_gemm_traffic(),
+            "traffic": measured_gemm_traffic() if a.workload == "fprop8b" else None,
         },
     }
-    if not a.no_cpu:
+    if w4a16:
+        result["dtype"] = "bf16 x nvfp4 (e2m1 x e4m3) -> exact bf16 operands, f32 accumulate"
+        result["components"] = {"gemm_ms": round(mm_ms, 4), "gemm_tflops": round(gemm_tflops, 1),
+                                "gemm_min_hbm_bytes": w4_bytes,
+                                "gemm_gbps": round(w4_bytes / (mm_ms * 1e-3) / 1e9, 1),
+                                "step_timing": "HIP graph replay of the W4A16 GEMM; gemm_ms: mean of back-to-back launches"}
+        result["roofline"]["kernel"] = "nvfp4 w4a16 gemm"
+        if a.workload == "w4a16_decode":
+            gbps = w4_bytes / (mm_ms * 1e-3) / 1e9
+            result["roofline"].update({"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                                       "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)})
+    if not a.no_cpu and not w4a16:
         result["cpu_baseline"] = cpu_baseline(a, nv)
     print(json.dumps(result), flush=True)
 

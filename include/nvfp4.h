@@ -162,6 +162,22 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  * overlap.  Runs on hip_stream and returns after the enqueue. */
 int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream);
 
+/* Weight-only 4-bit GEMM, bf16 activations x NVFP4 weights with FP32 accumulation (the W4A16 mode
+ * that a serving stack falls back to where the hardware has no FP4 x FP4 product: hyper.ai (de)
+ * story on the Nemotron 3 Ultra NVFP4 checkpoint, Hopper):
+ *   C[i][j] = ts_b * sum_k a[i][k] * (q_b[j][k] * S_b(j,k)),
+ * i.e. C = A * B^T with A [M x K] bf16 row-major (leading dimension lda elements) and B [N x K] = b
+ * (N = b->rows, K = b->k, 1D or BLOCK2D scales).  Each weight element q*S is exact in bf16, each
+ * product a*q*S exact in fp32, the K sum accumulates in fp32, and ts_b is applied once at the end.
+ * a_dtype must be NVFP4_BF16 (else NVFP4_ERR_UNSUPPORTED).  c: device, [M x N] with leading
+ * dimension ldc >= N, dtype NVFP4_F32 or NVFP4_BF16 (nearest-even).  K % 64 == 0 (else
+ * NVFP4_ERR_SHAPE); a and b->data 16-byte aligned, lda * 2 a multiple of 16 bytes, b->scales
+ * 4-byte aligned, c aligned to its element size (else NVFP4_ERR_ALIGN).  All buffers are device
+ * memory owned by the caller; c must not overlap the inputs.  Runs on hip_stream and returns after
+ * the enqueue. */
+int nvfp4_gemm_w4a16(const void *a, int a_dtype, int64_t m, int64_t lda, const nvfp4_tensor *b, void *c,
+                     int c_dtype, int64_t ldc, void *hip_stream);
+
 /* Static, human-readable text for a status code. */
 const char *nvfp4_status_string(int status);
 

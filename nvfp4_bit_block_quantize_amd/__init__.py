@@ -24,7 +24,7 @@ __all__ = [
     "NVFP4_ERR_HIP", "NVFP4_F32", "NVFP4_BF16", "NVFP4_COLWISE", "NVFP4_BLOCK2D", "NVFP4_SR",
     "NVFP4_FOUR_OVER_SIX", "NVFP4_TS_FOR_FOUR", "NVFP4_SCALE_SEARCH", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
     "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize",
-    "nvfp4_gemm", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
+    "nvfp4_gemm", "nvfp4_gemm_w4a16", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
 ]
 
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_HIP = range(6)
@@ -66,6 +66,8 @@ def lib():
         L.nvfp4_dequantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [TP, TP, P, ctypes.c_int, i64, i32, ctypes.POINTER(ctypes.c_int64), P]
         L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_gemm_w4a16.argtypes = [P, ctypes.c_int, i64, i64, TP, P, ctypes.c_int, i64, P]
+        L.nvfp4_gemm_w4a16.restype = ctypes.c_int
         L.nvfp4_transpose.argtypes = [TP, TP, P]
         L.nvfp4_transpose.restype = ctypes.c_int
         L.nvfp4_status_string.argtypes = [ctypes.c_int]
@@ -216,6 +218,26 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype: torch.dtype = torch.bf
     st = lib().nvfp4_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(out), _dtype_code(out.dtype), _ld(out), G, offs,
                           _stream_handle(out.device))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def nvfp4_gemm_w4a16(a: torch.Tensor, b: NVFP4Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A @ B_hat^T with A a bf16 [M x K] device matrix (unit stride along K) and B an NVFP4
+    weight [N x K]; FP32 accumulation (see include/nvfp4.h)."""
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("nvfp4_gemm_w4a16: A must be 2-D with unit stride along K")
+    if a.dtype != torch.bfloat16:
+        raise TypeError("nvfp4_gemm_w4a16: A must be bfloat16")
+    M, N = a.shape[0], b.rows
+    if a.shape[1] != b.k:
+        raise ValueError(f"nvfp4_gemm_w4a16: A has K={a.shape[1]}, B has K={b.k}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    db = b.descriptor()
+    st = lib().nvfp4_gemm_w4a16(_ptr(a), NVFP4_BF16, M, _ld(a), ctypes.byref(db), _ptr(out),
+                                _dtype_code(out.dtype), _ld(out), _stream_handle(out.device))
+    _check(st, "nvfp4_gemm_w4a16")
     return out
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libnvfp4.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["nvfp4_api.cpp", "quantize.hip", "dequant.hip", "gemm.hip", "transpose.hip"]
+SOURCES = ["nvfp4_api.cpp", "quantize.hip", "dequant.hip", "gemm.hip", "gemm_w4a16.hip", "transpose.hip"]
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",

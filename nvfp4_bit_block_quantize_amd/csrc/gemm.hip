@@ -20,6 +20,7 @@
 // (the XOR swizzles give conflict-free ds_read_b128 for eight consecutive rows).  Within a step,
 // lane half h of a 32-row MFMA fragment takes codes [64h, 64h + 64) of the step and MFMA m = 0..7
 // consumes its dword m; A and B use the same K assignment, which is all the product needs.
+#include "gemm_common.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -27,9 +28,9 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr uint32_t kThreads = 256;
+using namespace gemm;
+
 constexpr int kMaxGroupsPerLaunch = 128;
-constexpr int BM = 256, BN = 256;  // workgroup tile
 constexpr int BKB = 64;            // bytes of codes per row per K step (128 codes)
 constexpr int kCodeBytes = BM * BKB;        // one operand's codes per stage (16 KB)
 constexpr int kScaleBytes = BM * 8 * 4;     // one operand's fp16-pair scales per stage (8 KB)
@@ -37,7 +38,6 @@ constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;  // A + B
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct GemmKArgs {
   const uint8_t *a_data, *a_scales;
@@ -171,13 +171,6 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint8_t *codes, uin
   *reinterpret_cast<uint4 *>(scales + r * 32 + 16 * (1 ^ sw)) = h1;
 }
 
-// Map a workgroup id to a tile so that each of the 8 XCDs (workgroup i runs on XCD i % 8) owns a
-// contiguous range of tiles.
-__device__ __forceinline__ int32_t xcd_tile(int32_t wg, int32_t total) {
-  if (total % 8 != 0) return wg;
-  return (wg & 7) * (total >> 3) + (wg >> 3);
-}
-
 template <bool OUT_BF16, bool A2D, bool B2D, bool FULL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
@@ -188,16 +181,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
   while (g + 1 < p.groups && p.tile_begin[g + 1] <= tile) ++g;
   const int32_t local = tile - p.tile_begin[g];
   const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
-  // walk tiles in bands of 8 tile rows: neighbouring workgroups share A rows and B columns in L2
   int32_t tm, tn;
-  {
-    const int32_t band = 8;
-    const int32_t per_band = band * p.tiles_n;
-    const int32_t bi = local / per_band, rem = local - bi * per_band;
-    const int32_t rows_in_band = min(band, tiles_m_g - bi * band);
-    tn = rem / rows_in_band;
-    tm = bi * band + (rem - tn * rows_in_band);
-  }
+  band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
   const int64_t row_end = p.row_begin[g + 1];
   const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
@@ -342,33 +327,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
 constexpr int kPA = 0, kPB = 16384, kPSA = 32768, kPSB = 34816, kPStage = 36864;  // stage layout (bytes)
 constexpr int kLoadsPerStage = 12;  // direct loads issued per lane per stage
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void global_void;
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void lds_load16(const uint8_t *g, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const uint8_t *g, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) / lgkmcnt(0) only (the other counters left alone); gfx9 encoding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier that the compiler may not move memory accesses across; the caller has issued
-// the waits that make its own LDS traffic complete.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Chunk c (16 B) of tile row r is stored at position c ^ swz(r) of its 64-byte row: 8 or 16
 // consecutive rows reading the same chunk touch distinct 16-byte bank groups of a 128- or 256-byte
 // bank line, so a ds_read_b128 of a fragment is conflict-free.
@@ -386,16 +344,6 @@ __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t pick(const uint4 &v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// fp32 -> bf16, nearest-even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  const uint32_t b = __float_as_uint(v);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 template <bool OUT_BF16, bool A2D, bool B2D>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kPStage];
@@ -407,14 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
   const int32_t local = tile - p.tile_begin[g];
   const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
   int32_t tm, tn;
-  {
-    const int32_t band = 8;
-    const int32_t per_band = band * p.tiles_n;
-    const int32_t bi = local / per_band, rem = local - bi * per_band;
-    const int32_t rows_in_band = min(band, tiles_m_g - bi * band);
-    tn = rem / rows_in_band;
-    tm = bi * band + (rem - tn * rows_in_band);
-  }
+  band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
   const int64_t row_end = p.row_begin[g + 1];
   const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
@@ -581,68 +522,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
     tgt = done;
   }
 
-  // ---- epilogue: lane holds row l32 of each 32 x 32 tile, columns 8 (r >> 2) + 4 h + (r & 3).
-  // Whole tiles go through LDS, 32 rows of the wave's quarter at a time, so that each store writes
-  // 16 consecutive bytes per lane and four (bf16) or two (fp32) complete 256 / 512-byte row segments
-  // per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row).
+  // ---- epilogue
   const float ts = *p.a_ts * p.b_ts[p.group_base + g];
-  constexpr int64_t ES = OUT_BF16 ? 2 : 4;
-  if (p.vec_store && m0 + BM <= row_end && n0 + BN <= p.N) {
-    // all waves are done with the stages and the last (re-fetch) loads have landed
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    lds_barrier();
-    constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
-    uint8_t *const region = smem + wave * (32 * ROWB);
-    uint8_t *const gbase = p.c + ((m0 + wm) * p.ldc + n0 + wn) * ES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v0 = acc[j][i][4 * q] * ts, v1 = acc[j][i][4 * q + 1] * ts;
-          const float v2 = acc[j][i][4 * q + 2] * ts, v3 = acc[j][i][4 * q + 3] * ts;
-          if constexpr (OUT_BF16) {
-            // v_cvt_pk_bf16_f32: nearest-even, as the integer rounding used elsewhere in this file
-            const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
-            const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
-            const uint32_t c = 4 * j + q;
-            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((c ^ (l32 & 15)) * 16 + 8 * h)) =
-                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-          } else {
-            const uint32_t c = 8 * j + 2 * q + h;
-            *reinterpret_cast<float4 *>(region + l32 * ROWB + (c ^ (l32 & 31)) * 16) = make_float4(v0, v1, v2, v3);
-          }
-        }
-      // the wave reads back its own rows (LDS accesses of one wave complete in order)
-#pragma unroll
-      for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
-        const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
-        const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
-        *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * p.ldc * ES + u * 16) = v;
-      }
-    }
-  } else {
-    const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = row0 + 32 * i;
-      if (row >= row_end) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
-          if (col >= p.N) continue;
-          const float v = acc[j][i][r] * ts;
-          if constexpr (OUT_BF16)
-            reinterpret_cast<uint16_t *>(p.c + row * p.ldc * 2)[col] = static_cast<uint16_t>(bf16_rne(v));
-          else
-            reinterpret_cast<float *>(p.c + row * p.ldc * 4)[col] = v;
-        }
-    }
-  }
+  store_c_tile<OUT_BF16>(acc, smem, p.c, p.ldc, m0, n0, row_end, p.N, ts, p.vec_store != 0, wave, lane);
 }
 
 }  // namespace
@@ -684,7 +566,9 @@ hipError_t launch_gemm(const GemmArgs &a) {
     const bool bf16 = a.c_dtype == 1;
     p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % 16) == 0 && ((a.ldc * (bf16 ? 2 : 4)) % 16) == 0;
     // whole K steps and 8-byte aligned scale rows: branch-free loads
-    const bool full = (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
+    // (K == 0 takes the generic kernel, whose loads are guarded: the ring's prologue would read the
+    // clamped step -1)
+    const bool full = a.K > 0 && (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0;
 #define NVFP4_GEMM(OB, A2, B2)                                                                            \
   do {                                                                                                   \

@@ -1,0 +1,148 @@
+// gemm_common.hpp -- pieces shared by the MFMA GEMM kernels (NVFP4 x NVFP4 and bf16 x NVFP4): the
+// 256 x 256 workgroup tile with four 128 x 128 wave quarters, direct global->LDS loads, the explicit
+// waits and barrier of the LDS ring, the tile order, and the LDS-staged epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace nvfp4 {
+namespace gemm {
+
+constexpr uint32_t kThreads = 256;
+constexpr int BM = 256, BN = 256;  // workgroup tile
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Direct global->LDS loads: lane l of the instruction writes its 16 (4) bytes at lds_base + 16 l
+// (4 l); lds_base must be the same in every lane.
+__device__ __forceinline__ void lds_load16(const uint8_t *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const uint8_t *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((global_void *)g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) / lgkmcnt(0) only (the other counters left alone); gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that the compiler may not move memory accesses across; the caller has issued
+// the waits that make its own LDS traffic complete.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// fp32 -> bf16, nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Map a workgroup id to a tile so that each of the 8 XCDs (workgroup i runs on XCD i % 8) owns a
+// contiguous range of tiles.
+__device__ __forceinline__ int32_t xcd_tile(int32_t wg, int32_t total) {
+  if (total % 8 != 0) return wg;
+  return (wg & 7) * (total >> 3) + (wg >> 3);
+}
+
+// Tile index -> (tile row, tile column), walking bands of 8 tile rows column by column, so that the
+// tiles in flight together share their B columns and a few A rows in L2.
+__device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_t tiles_m, int32_t &tm,
+                                          int32_t &tn) {
+  const int32_t band = 8;
+  const int32_t per_band = band * tiles_n;
+  const int32_t bi = local / per_band, rem = local - bi * per_band;
+  const int32_t rows_in_band = min(band, tiles_m - bi * band);
+  tn = rem / rows_in_band;
+  tm = bi * band + (rem - tn * rows_in_band);
+}
+
+// Epilogue of a 256 x 256 tile: C = ts * acc, where acc[j][i] is the 32 x 32 product of the wave's
+// B fragment j and A fragment i, so lane (h, l32) holds row l32 of tile (i, j), columns
+// 8 (r >> 2) + 4 h + (r & 3).  Whole tiles go through LDS (smem, at least 4 x 32 x 512 bytes, no
+// longer read by any wave's pending loads), 32 rows of the wave's quarter at a time, so that each
+// store writes 16 consecutive bytes per lane and four (bf16) or two (fp32) complete 256 / 512-byte
+// row segments per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row).
+// Partial tiles, or C without 16-byte aligned rows, take element stores.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
+                                             int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts,
+                                             bool vec_store, uint32_t wave, uint32_t lane) {
+  constexpr int64_t ES = OUT_BF16 ? 2 : 4;
+  const uint32_t h = lane >> 5, l32 = lane & 31u;
+  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  if (vec_store && m0 + BM <= row_end && n0 + BN <= N) {
+    // all waves are done with the stages and the last (re-fetch) loads have landed
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    lds_barrier();
+    constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
+    uint8_t *const region = smem + wave * (32 * ROWB);
+    uint8_t *const gbase = c + ((m0 + wm) * ldc + n0 + wn) * ES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = acc[j][i][4 * q] * ts, v1 = acc[j][i][4 * q + 1] * ts;
+          const float v2 = acc[j][i][4 * q + 2] * ts, v3 = acc[j][i][4 * q + 3] * ts;
+          if constexpr (OUT_BF16) {
+            // v_cvt_pk_bf16_f32: nearest-even, as bf16_rne
+            const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
+            const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
+            const uint32_t ch = 4 * j + q;
+            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((ch ^ (l32 & 15)) * 16 + 8 * h)) =
+                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          } else {
+            const uint32_t ch = 8 * j + 2 * q + h;
+            *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & 31)) * 16) = make_float4(v0, v1, v2, v3);
+          }
+        }
+      // the wave reads back its own rows (LDS accesses of one wave complete in order)
+#pragma unroll
+      for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
+        const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
+        const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
+        *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * ldc * ES + u * 16) = v;
+      }
+    }
+  } else {
+    const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + 32 * i;
+      if (row >= row_end) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
+          if (col >= N) continue;
+          const float v = acc[j][i][r] * ts;
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t *>(c + row * ldc * 2)[col] = static_cast<uint16_t>(bf16_rne(v));
+          else
+            reinterpret_cast<float *>(c + row * ldc * 4)[col] = v;
+        }
+    }
+  }
+}
+
+}  // namespace gemm
+}  // namespace nvfp4

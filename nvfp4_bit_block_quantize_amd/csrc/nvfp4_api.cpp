@@ -170,9 +170,11 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
       if (group_row_offsets[g + 1] < group_row_offsets[g]) return NVFP4_ERR_SHAPE;
   }
   if (M == 0 || N == 0) return NVFP4_OK;
-  if (!a->data || !a->scales || !a->tensor_scale || !b->data || !b->scales || !b->tensor_scale || !c)
-    return NVFP4_ERR_NULL;
-  if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
+  if (!a->tensor_scale || !b->tensor_scale || !c) return NVFP4_ERR_NULL;
+  if (K > 0) {  // (with K == 0 no code or scale is read and C = 0)
+    if (!a->data || !a->scales || !b->data || !b->scales) return NVFP4_ERR_NULL;
+    if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
+  }
   if ((reinterpret_cast<uintptr_t>(c) & static_cast<uintptr_t>(dtype_size(c_dtype) - 1)) != 0) return NVFP4_ERR_ALIGN;
   nvfp4::GemmArgs g{};
   g.a_data = a->data;
@@ -193,6 +195,40 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
   g.group_offsets = group_row_offsets;
   g.stream = static_cast<hipStream_t>(hip_stream);
   return status_of(nvfp4::launch_gemm(g));
+}
+
+int nvfp4_gemm_w4a16(const void *a, int a_dtype, int64_t m, int64_t lda, const nvfp4_tensor *b, void *c,
+                     int c_dtype, int64_t ldc, void *hip_stream) {
+  if (!b) return NVFP4_ERR_NULL;
+  if (a_dtype != NVFP4_BF16 || dtype_size(c_dtype) == 0) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t M = m, N = b->rows, K = b->k;
+  if (M < 0 || N < 0 || K < 0 || K % 64 != 0 || lda < K || lda < 1 || ldc < N || ldc < 1) return NVFP4_ERR_SHAPE;
+  if ((b->flags & NVFP4_BLOCK2D) && N % 16 != 0) return NVFP4_ERR_SHAPE;
+  // byte offsets into A and B are 32-bit in the kernel
+  if (M * lda >= kMaxIndex / 2 || N * K >= kMaxIndex || M * ldc >= kMaxIndex * 4) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!b->tensor_scale || !c) return NVFP4_ERR_NULL;
+  if (K > 0) {  // (with K == 0 nothing of A or B is read and C = 0)
+    if (!a || !b->data || !b->scales) return NVFP4_ERR_NULL;
+    if (!aligned16(a) || (lda * 2) % 16 != 0 || !aligned16(b->data) || (reinterpret_cast<uintptr_t>(b->scales) & 3u) != 0)
+      return NVFP4_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(c) & static_cast<uintptr_t>(dtype_size(c_dtype) - 1)) != 0) return NVFP4_ERR_ALIGN;
+  nvfp4::W4A16Args w{};
+  w.a = a;
+  w.lda = lda;
+  w.b_data = b->data;
+  w.b_scales = b->scales;
+  w.b_ts = b->tensor_scale;
+  w.b_2d = (b->flags & NVFP4_BLOCK2D) != 0;
+  w.M = M;
+  w.N = N;
+  w.K = K;
+  w.c = c;
+  w.c_dtype = c_dtype == NVFP4_BF16 ? 1 : 0;
+  w.ldc = ldc;
+  w.stream = static_cast<hipStream_t>(hip_stream);
+  return status_of(nvfp4::launch_gemm_w4a16(w));
 }
 
 int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream) {

@@ -56,6 +56,19 @@ struct GemmArgs {
   hipStream_t stream;
 };
 
+struct W4A16Args {
+  const void *a;  // bf16 [M x lda]
+  int64_t lda;    // elements
+  const uint8_t *b_data, *b_scales;
+  const float *b_ts;
+  bool b_2d;
+  int64_t M, N, K;
+  void *c;
+  int c_dtype;
+  int64_t ldc;
+  hipStream_t stream;
+};
+
 struct TransposeLaunch {
   const uint8_t *in_data, *in_scales;
   const float *in_ts;
@@ -70,6 +83,7 @@ hipError_t launch_quantize(const QuantArgs &a);
 hipError_t launch_dequantize(const DequantArgs &a);
 hipError_t launch_gemm(const GemmArgs &a);
 hipError_t launch_transpose(const TransposeLaunch &a);
+hipError_t launch_gemm_w4a16(const W4A16Args &a);
 
 // Host copy of the Philox4x32-10 block function (for the RHT sign word).
 void philox4x32_10_host(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);

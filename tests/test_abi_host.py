@@ -132,3 +132,28 @@ def test_transpose_validation():
     assert t(_desc(32, 64, B2), _desc(32, 64, B2)) == nv.NVFP4_ERR_SHAPE        # out must be [k x rows]
     assert t(_desc(40, 64, B2), _desc(64, 40, B2)) == nv.NVFP4_ERR_SHAPE        # rows % 16
     assert t(_desc(32, 64, B2, data=MIS), _desc(64, 32, B2)) == nv.NVFP4_ERR_ALIGN
+
+
+def test_gemm_w4a16_validation():
+    L = nv.lib()
+    b = _desc(32, 128)
+    g = lambda a=FAKE, adt=nv.NVFP4_BF16, m=64, lda=128, b_=b, c=FAKE, dt=1, ldc=32: L.nvfp4_gemm_w4a16(
+        a, adt, m, lda, ctypes.byref(b_) if b_ else None, c, dt, ldc, None)
+    assert g(b_=None) == nv.NVFP4_ERR_NULL
+    assert g(adt=nv.NVFP4_F32) == nv.NVFP4_ERR_UNSUPPORTED       # activations are bf16
+    assert g(dt=5) == nv.NVFP4_ERR_UNSUPPORTED
+    assert g(b_=_desc(32, 96), lda=96) == nv.NVFP4_ERR_SHAPE     # K % 64
+    assert g(lda=64) == nv.NVFP4_ERR_SHAPE                       # lda < K
+    assert g(ldc=16) == nv.NVFP4_ERR_SHAPE                       # ldc < N
+    assert g(m=-1) == nv.NVFP4_ERR_SHAPE
+    assert g(b_=_desc(40, 128, nv.NVFP4_BLOCK2D)) == nv.NVFP4_ERR_SHAPE
+    assert g(m=1 << 24, lda=1 << 8) == nv.NVFP4_ERR_SHAPE        # A beyond 32-bit byte offsets
+    assert g(a=None) == nv.NVFP4_ERR_NULL
+    assert g(c=None) == nv.NVFP4_ERR_NULL
+    assert g(a=MIS) == nv.NVFP4_ERR_ALIGN
+    assert g(lda=132) == nv.NVFP4_ERR_ALIGN                      # rows of A not 16-byte aligned
+    assert g(b_=_desc(32, 128, data=MIS)) == nv.NVFP4_ERR_ALIGN
+    assert g(b_=_desc(32, 128, scales=FAKE + 2)) == nv.NVFP4_ERR_ALIGN
+    assert g(c=FAKE + 1) == nv.NVFP4_ERR_ALIGN
+    assert g(m=0) == nv.NVFP4_OK                                 # empty: no-op
+    assert g(b_=_desc(0, 128)) == nv.NVFP4_OK
