@@ -59,7 +59,7 @@ def gemm_source_digest():
     """sha256 over the GEMM kernel sources (the counters below are only valid for this source)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "nvfp4_device.hpp"):
+    for f in ("gemm.hip", "gemm_common.hpp", "nvfp4_device.hpp"):
         with open(os.path.join(ROOT, "nvfp4_bit_block_quantize_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -241,9 +241,245 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(W4Args p) {
   store_c_tile<OUT_BF16>(acc, smem, p.c, p.ldc, m0, n0, p.M, p.N, *p.b_ts, p.vec_store != 0, wave, lane);
 }
 
+// ---- few activation rows (decode): weight streaming --------------------------------------------------
+// With M <= 64 the product is bound by reading the weight once from HBM.  A workgroup of W waves owns
+// 64 weight rows (four 16-row tiles) and all M <= 16 MT activation rows; its waves split K, wave w
+// taking the 128-element chunks w, w + W, ... (neighbouring waves read neighbouring bytes of each row),
+// and their partial sums meet in LDS at the end.
+// Per chunk and lane (n = l & 15, g = l >> 4):
+//   - the weight tile's codes arrive as one 16-byte load per lane (row n, codes [32 g, 32 g + 32)),
+//     i.e. dword j holds K offsets 32 g + 8 j; a 4 x 4 transpose across the four 16-lane rows
+//     (v_permlane32_swap, then v_permlane16_swap) gives dword t = K offsets 32 t + 8 g;
+//   - the activation chunk (16 MT rows x 256 bytes) arrives lane-contiguously (load t of M tile mt: rows
+//     16 mt + 4 t + (l >> 4), 16-byte piece l & 15), passes through a wave-private LDS buffer (piece j
+//     of row r at position j ^ (r & 15): conflict-free both ways) and is read back as MFMA fragments:
+//     row m = l & 15, piece 4 t + g = K offsets 32 t + 8 g;
+//   - MFMA t (v_mfma_f32_16x16x32_bf16) consumes K offsets {32 t + 8 g + e}: the same set on both sides.
+// The block scale of (t, g) is block 2 t + (g >> 1) of the chunk's eight.
+constexpr int kSkRows = 64;
+// buffer resource word 3 for gfx9-family raw buffer loads (32-bit data format), and a byte offset
+// beyond any buffer used here (each is below 2 GiB)
+constexpr int32_t kBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kSkRed = 4 * 64 + 16;  // floats per (wave, M tile, weight tile) partial (padded)
+
+struct SkArgs {
+  const uint8_t *a;
+  int64_t lda_bytes;
+  int64_t M;
+  const uint8_t *b_data, *b_scales;
+  const float *b_ts;
+  int64_t N, K;
+  uint8_t *c;
+  int64_t ldc;
+};
+
+template <int MT>
+struct SkChunk {
+  uint4 b[4];       // codes of the four weight tiles (before the transpose)
+  uint2 s[4];       // the chunk's eight scale bytes per tile row
+  uint4 a[MT][4];   // activation rows, lane-contiguous
+};
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int MT, int W, int R, bool OUT_BF16, bool B2D>
+__global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) {
+  __shared__ float red[W * MT * 4 * kSkRed];
+  __shared__ __attribute__((aligned(16))) uint8_t a_tr[W][16 * MT * 256];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t n16 = lane & 15u, g = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kSkRows;
+  const int64_t KC = p.K / 128, KB = p.K / 16, row_bytes = p.K / 2;
+
+  // per-lane sources: 32-bit byte offsets of chunk 0 (each operand is below 4 GiB)
+  uint32_t srcB[4], srcS[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t n = min(n0 + 16 * nt + n16, p.N - 1);
+    srcB[nt] = static_cast<uint32_t>(n * row_bytes + 16 * g);
+    srcS[nt] = static_cast<uint32_t>(B2D ? (n / 16) * KB : n * KB);
+  }
+  // activation rows 16 mt + 4 t + (l >> 4), clamped to the last row (their sums are never stored)
+  const uint32_t a_last = static_cast<uint32_t>(p.M - 1), a_r0 = lane >> 4, a_piece = 16 * (lane & 15);
+  const uint32_t lda_b = static_cast<uint32_t>(p.lda_bytes);
+  // v_perm selector picking scale bytes 2 t + (g >> 1), t = 0..3, out of the chunk's eight
+  const uint32_t sh = g >> 1;
+  const uint32_t ssel = sh | ((2 + sh) << 8) | ((4 + sh) << 16) | ((6 + sh) << 24);
+
+  // Loads are buffer loads: a chunk index past this wave's last turns into an offset beyond the
+  // buffer, which the hardware answers with zeros and no memory access.  So every iteration issues
+  // the same loads (the wait counts stay exact) and a padding chunk adds zeros.
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(p.b_data), 0, static_cast<int32_t>(p.N * row_bytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(p.b_scales), 0, static_cast<int32_t>((B2D ? (p.N + 15) / 16 : p.N) * KB), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(p.a), 0, static_cast<int32_t>((p.M - 1) * p.lda_bytes + 2 * p.K), kBufferWord3);
+  auto load = [&](SkChunk<MT> &ch, int64_t c, bool valid) {
+    const uint32_t ob = valid ? static_cast<uint32_t>(c * 64) : kOutOfRange;
+    const uint32_t os = valid ? static_cast<uint32_t>(c * 8) : kOutOfRange;
+    const uint32_t oa = valid ? static_cast<uint32_t>(c * 256) : kOutOfRange;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      ch.b[nt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, srcB[nt] + ob, 0, 0));
+      ch.s[nt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs_s, srcS[nt] + os, 0, 0));
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        ch.a[mt][t] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, min(16 * mt + 4 * t + a_r0, a_last) * lda_b + a_piece + oa, 0, 0));
+  };
+  // activation chunk -> this wave's LDS buffer -> MFMA fragments (see above)
+  uint8_t *const tr = a_tr[wave];
+  const uint32_t rd_row = 256 * n16;
+  auto fragments = [&](const SkChunk<MT> &ch, uint4 (&af)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // row 16 mt + 4 t + (l >> 4): (row & 15) = 4 t + (l >> 4)
+        const uint32_t row = 16 * mt + 4 * t + (lane >> 4);
+        *reinterpret_cast<uint4 *>(tr + 256 * row + (16 * ((lane & 15) ^ (4 * t + (lane >> 4))))) = ch.a[mt][t];
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        af[mt][t] = *reinterpret_cast<const uint4 *>(tr + 4096 * mt + rd_row + 16 * ((4 * t + g) ^ n16));
+  };
+
+  floatx4 acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const SkChunk<MT> &ch) {
+    uint4 af[MT][4];
+    fragments(ch, af);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      // 4 x 4 transpose of the tile's dwords across the lane rows g
+      uint32_t x0 = ch.b[nt].x, x1 = ch.b[nt].y, x2 = ch.b[nt].z, x3 = ch.b[nt].w;
+      {
+        const auto r02 = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+        const auto r13 = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+        const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+        const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+        x0 = r01[0];
+        x1 = r01[1];
+        x2 = r23[0];
+        x3 = r23[1];
+      }
+      const uint32_t sb = __builtin_amdgcn_perm(ch.s[nt].y, ch.s[nt].x, ssel);
+      const float2v s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false);
+      const float2v s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, true);
+      const bf16x8 w[4] = {decode8_bf16(x0, s01[0]), decode8_bf16(x1, s01[1]), decode8_bf16(x2, s23[0]),
+                           decode8_bf16(x3, s23[1])};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[mt][t]), w[t],
+                                                                acc[mt][nt], 0, 0, 0);
+    }
+  };
+
+  // this wave's chunks: wave, wave + W, ...; a ring of R register sets keeps the loads of R - 1 chunks
+  // in flight under the math (the scheduling barriers keep each chunk's loads ahead of the math
+  // before them).  The count is rounded up to a multiple of R; padding chunks load zeros.
+  const int64_t nch = wave < KC ? (KC - wave + W - 1) / W : 0;
+  {
+    auto chunk = [&](int64_t i) { return static_cast<int64_t>(wave) + W * i; };
+    SkChunk<MT> ring[R];
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) load(ring[j], chunk(j), j < nch);
+    for (int64_t i = 0; i < nch; i += R) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        load(ring[(j + R - 1) % R], chunk(i + j + R - 1), i + j + R - 1 < nch);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ring[j]);
+      }
+    }
+  }
+
+  // partial sums -> LDS; lane l of tile (mt, nt) holds rows 4 g + i, column n16
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((wave * MT + mt) * 4 + nt) * kSkRed + 64 * i + lane] = acc[mt][nt][i];
+  __syncthreads();
+  // thread (r = tid >> 6, col = tid & 63) sums rows r, r + W, ... of every M tile over the waves
+  const float ts = *p.b_ts;
+  const uint32_t col = threadIdx.x & 63u, r0 = threadIdx.x >> 6, nt = col >> 4;
+  const int64_t n = n0 + col;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 16 / W; ++h) {
+      const uint32_t mr = r0 + W * h;  // row within the M tile
+      const int64_t m = 16 * mt + mr;
+      const uint32_t off = (mt * 4 + nt) * kSkRed + 64 * (mr & 3) + (col & 15) + 16 * (mr >> 2);
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) v += red[w * MT * 4 * kSkRed + off];
+      v *= ts;
+      if (m < p.M && n < p.N) {
+        if constexpr (OUT_BF16)
+          reinterpret_cast<uint16_t *>(p.c + m * p.ldc * 2)[n] = static_cast<uint16_t>(bf16_rne(v));
+        else
+          reinterpret_cast<float *>(p.c + m * p.ldc * 4)[n] = v;
+      }
+    }
+}
+
+// Four waves (one per SIMD) and two chunks per ring: measured on the 16 x 14336 x 4096 decode shape,
+// eight waves or deeper rings were no faster (deeper rings delay every wave's first chunk)
+template <int MT>
+void launch_skinny(const W4A16Args &a, const SkArgs &p) {
+  constexpr int W = 4, R = 2;
+  const dim3 grid(static_cast<uint32_t>((a.N + kSkRows - 1) / kSkRows)), block(64 * W);
+  if (a.c_dtype == 1) {
+    if (a.b_2d) hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, true, true>), grid, block, 0, a.stream, p);
+    else hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, true, false>), grid, block, 0, a.stream, p);
+  } else {
+    if (a.b_2d) hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, false, true>), grid, block, 0, a.stream, p);
+    else hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, false, false>), grid, block, 0, a.stream, p);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const W4A16Args &a) {
+  // few activation rows, whole 128-element chunks, 8-byte aligned scale rows: weight streaming
+  if (a.M > 0 && a.M <= 64 && a.N > 0 && a.K > 0 && a.K % 128 == 0 &&
+      (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0 && (a.M - 1) * a.lda * 2 + 2 * a.K < (int64_t(1) << 31)) {
+    SkArgs p{};
+    p.a = static_cast<const uint8_t *>(a.a);
+    p.lda_bytes = a.lda * 2;
+    p.M = a.M;
+    p.b_data = a.b_data;
+    p.b_scales = a.b_scales;
+    p.b_ts = a.b_ts;
+    p.N = a.N;
+    p.K = a.K;
+    p.c = static_cast<uint8_t *>(a.c);
+    p.ldc = a.ldc;
+    switch ((a.M + 15) / 16) {
+      case 1: launch_skinny<1>(a, p); break;
+      case 2: launch_skinny<2>(a, p); break;
+      case 3: launch_skinny<3>(a, p); break;
+      default: launch_skinny<4>(a, p); break;
+    }
+    return hipGetLastError();
+  }
   const int32_t tiles_n = static_cast<int32_t>((a.N + BN - 1) / BN);
   const int32_t tiles_m = static_cast<int32_t>((a.M + BM - 1) / BM);
   if (tiles_n == 0 || tiles_m == 0) return hipSuccess;

@@ -50,6 +50,21 @@ def test_w4a16_ragged_shapes(oracle, M, N, K, out_dtype):
     print(f"max |err| / bound = {rel:.3e}")
 
 
+# few activation rows (<= 64) and K % 128 == 0 take the weight-streaming kernel: M tiles 1..4, chunk
+# counts that leave waves idle (K = 128) or uneven (K = 1152), ragged N, 1D and 2D scales
+@pytest.mark.parametrize("M,N,K", [(1, 200, 128), (5, 64, 1152), (16, 1000, 512), (17, 130, 2048),
+                                   (33, 64, 256), (64, 336, 1024), (65, 96, 256)])
+@pytest.mark.parametrize("b_flags", [0, 2])
+def test_w4a16_few_rows(oracle, M, N, K, b_flags):
+    if b_flags and N % 16:
+        pytest.skip("2D scales need N % 16 == 0")
+    a = synth.normal((M, K), 1.0, seed=10, tensor_id=88, dtype=torch.bfloat16)
+    w = synth.normal((N, K), 0.02, seed=10, tensor_id=89, dtype=torch.bfloat16)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        rel = _case(oracle, a, w, b_flags=b_flags, out_dtype=out_dtype, what=f"few rows {M}x{N}x{K}")
+    print(f"max |err| / bound = {rel:.3e}")
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_w4a16_2d_weight_scales(oracle, out_dtype):
     a = synth.normal((300, 640), 1.0, seed=6, tensor_id=82, dtype=torch.bfloat16)
