@@ -68,6 +68,8 @@ def lib():
                                   P, P, P, P, P, ctypes.c_int]
         L.or_quantize.restype = ctypes.c_int
         L.or_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, u32, P]
+        L.or_quantize_given_ts.argtypes = [P, i64, i64, i64, ctypes.c_float, P, P, ctypes.c_int]
+        L.or_quantize_given_ts.restype = ctypes.c_int
         L.or_dequantize.restype = ctypes.c_int
         L.or_gemm_ref.argtypes = [P, P, ctypes.c_float, u32, P, P, ctypes.c_float, u32,
                                   i64, i64, i64, P, i64, P, P, ctypes.c_int]
@@ -169,6 +171,21 @@ def quantize(x, flags=0, seed=0, stream_id=0, rht=False, sign_seed=0, want_rht_o
         raise ValueError(f"oracle quantize rejected the arguments (code {rc})")
     return {"data": data, "scales": scales, "ts": ts[0], "rht_out": rht_out,
             "sse": (float(sse[0]), float(sse[1])), "flags": flags, "R": R, "K": K}
+
+
+def quantize_given_ts(y, ts, nthreads=None):
+    """Row-wise 1D nearest-even quantization of float32 y [rows x cols] with the given tensor scale.
+    Returns (data [rows][cols/2] u8, scales [rows][cols/16] u8)."""
+    y = np.asarray(y)
+    assert y.dtype == np.float32 and y.ndim == 2 and y.strides[1] == 4
+    rows, cols = y.shape
+    data = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    rc = lib().or_quantize_given_ts(_p(y), rows, cols, y.strides[0] // 4, float(np.float32(ts)), _p(data), _p(scales),
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle quantize_given_ts rejected the arguments")
+    return data, scales
 
 
 def dequantize(data, scales, ts, R, K, flags=0):

@@ -414,6 +414,30 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
   return 0;
 }
 
+int or_quantize_given_ts(const float *y, int64_t rows, int64_t cols, int64_t ldy, float ts, uint8_t *data,
+                         uint8_t *scales, int nthreads) {
+  if (cols % 16 != 0 || rows < 0 || ldy < cols) return 2;
+  const int64_t KB = cols / 16;
+  QuantCtx c{rows, cols, 0u, 0u, 0u, ts};
+  parallel_ranges(rows, 1, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      for (int64_t kb = 0; kb < KB; ++kb) {
+        const float *blk = y + r * ldy + 16 * kb;
+        float ab = 0.0f;
+        for (int t = 0; t < 16; ++t) ab = std::max(ab, std::fabs(blk[t]));
+        const uint8_t sb = block_scale_byte(ab, 6.0f, ts);
+        scales[r * KB + kb] = sb;
+        for (int t = 0; t < 16; t += 2) {
+          const uint8_t lo_code = encode_element(c, blk[t], sb, r, 16 * kb + t);
+          const uint8_t hi_code = encode_element(c, blk[t + 1], sb, r, 16 * kb + t + 1);
+          data[r * (cols / 2) + 8 * kb + t / 2] = static_cast<uint8_t>(lo_code | (hi_code << 4));
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 int or_dequantize(const uint8_t *data, const uint8_t *scales, float ts, int64_t R, int64_t K,
                   uint32_t flags, float *y) {
   if (K % 16 != 0) return 2;

@@ -83,6 +83,16 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
                 uint8_t *data, uint8_t *scales, float *ts, float *rht_out, double *sse2,
                 int nthreads);
 
+/* Row-wise 1D nearest-even quantization of an fp32 matrix y [rows][ldy] with a GIVEN tensor scale
+ * ts (instead of amax / 2688): the same per-block steps as or_quantize with flags 0 (block scale
+ * RN(RN(a_b / 6) / ts) clamped to 448 then E4M3 nearest-even; e = RN(1 / RN(S * ts)); codes the
+ * nearest E2M1 value of |y| * e, ties to even, saturating at 6; ts == 0 gives zero scales and
+ * signed-zero codes).  This is what a GEMM epilogue that quantizes its output under delayed
+ * scaling computes (the tensor scale comes from an earlier maximum; this library's reading).
+ * data [rows][cols/2], scales [rows][cols/16].  Returns 0, or 2 if cols % 16 != 0.            */
+int or_quantize_given_ts(const float *y, int64_t rows, int64_t cols, int64_t ldy, float ts, uint8_t *data,
+                         uint8_t *scales, int nthreads);
+
 /* Dequantize to fp32: y[r*K + k] = RN(RN(e2m1 * S) * ts). */
 int or_dequantize(const uint8_t *data, const uint8_t *scales, float ts, int64_t R, int64_t K,
                   uint32_t flags, float *y);
