@@ -34,7 +34,7 @@ def _args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop8b",
-                   choices=["fprop8b", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode"])
+                   choices=["fprop8b", "fprop8b_q", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode"])
     p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
@@ -154,13 +154,16 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return
 
-    if a.workload == "fprop8b":
+    if a.workload in ("fprop8b", "fprop8b_q"):
         x_cpu, w_cpu = synth.fprop8b(0)
         M, K = x_cpu.shape
         N = w_cpu.shape[0]
         fa, fb, rht = 0, nv.NVFP4_BLOCK2D, False
         out_dtype = torch.bfloat16
         workload = "Llama-3-8B FFN fprop: X[8192x4096] bf16 1D blocks, W[14336x4096] bf16 16x16 tiles, Y bf16"
+        if a.workload == "fprop8b_q":
+            workload = ("Llama-3-8B FFN fprop: X[8192x4096] bf16 1D blocks, W[14336x4096] bf16 16x16 tiles, "
+                        "Y quantized to NVFP4 (1D) in the GEMM epilogue, tensor scale from the previous step's amax")
         qbytes = quant_bytes(M, K, False) + quant_bytes(N, K, True)
     elif a.workload == "dgrad8b":
         dy_cpu, _ = synth.wgrad8b(0)
@@ -213,6 +216,10 @@ def main():
     y = torch.empty((M, N), dtype=out_dtype, device=dev)
 
     w4a16 = a.workload.startswith("w4a16")
+    fused = a.workload == "fprop8b_q"
+    if fused:
+        y_q = nv.empty_like_quantized(M, N, 0, dev)
+        amax = torch.zeros(1, dtype=torch.float32, device=dev)
     if w4a16:
         qb = nv.nvfp4_quantize(w, flags=fb, workspace=ws_b)
 
@@ -235,13 +242,20 @@ def main():
             nv.nvfp4_quantize(w, flags=fb, out=qb, workspace=ws_b)
 
     def mm():
-        if w4a16:
+        if fused:
+            nv.nvfp4_gemm_nvfp4_out(qa, qb, y_q, amax=amax)
+        elif w4a16:
             nv.nvfp4_gemm_w4a16(x, qb, out=y)
         else:
             nv.nvfp4_gemm(qa, qb, out=y)
 
     def step():
-        q_a(); q_b(); mm()
+        q_a(); q_b()
+        if fused:
+            # delayed scaling: this step's tensor scale from the previous step's amax
+            nv.nvfp4_scale_from_amax(amax, y_q.tensor_scale)
+            amax.zero_()
+        mm()
 
     for _ in range(a.warmup):
         step()
@@ -261,12 +275,22 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) / a.steps
 
+    unfused_ms = None
+    if fused:
+        # the same output the unfused way: bf16 Y, then its two-pass quantization
+        ws_y = torch.empty(nv.nvfp4_workspace_size(M, N, 0) // 4, dtype=torch.int32, device=dev)
+        y_q2 = nv.empty_like_quantized(M, N, 0, dev)
+
+        def unfused():
+            nv.nvfp4_gemm(qa, qb, out=y)
+            nv.nvfp4_quantize(y, out=y_q2, workspace=ws_y)
+        unfused_ms = per_call_ms(unfused)
     qa_ms = per_call_ms(q_a) if not w4a16 else 0.0
     qb_ms = per_call_ms(q_b) if not w4a16 else 0.0
     mm_ms = per_call_ms(mm)
     step()
     torch.cuda.synchronize()
-    y_eager = y.clone()
+    y_eager = y.clone() if not fused else torch.cat([y_q.data.view(-1), y_q.scales.view(-1)])
 
     # the step as one HIP graph (every library call is capturable: kernels only, no memsets)
     graph = torch.cuda.CUDAGraph()
@@ -280,7 +304,8 @@ def main():
         step()
     graph.replay()
     torch.cuda.synchronize()
-    graph_ok = bool(torch.equal(y, y_eager))
+    graph_ok = bool(torch.equal(y, y_eager)) if not fused else bool(
+        torch.equal(torch.cat([y_q.data.view(-1), y_q.scales.view(-1)]), y_eager))
     if not graph_ok:
         print(json.dumps({"error": "graph replay differs from eager result"}))
         sys.exit(1)
@@ -335,6 +360,10 @@ def main():
             "traffic": measured_gemm_traffic() if a.workload == "fprop8b" else None,
         },
     }
+    if fused:
+        result["components"]["unfused_gemm_bf16_plus_quantize_ms"] = round(unfused_ms, 4)
+        result["components"]["step_timing"] = ("HIP graph replay of quantize(A) + quantize(B) + tensor scale from "
+                                               "the previous amax + GEMM with NVFP4 output")
     if w4a16:
         result["dtype"] = "bf16 x nvfp4 (e2m1 x e4m3) -> exact bf16 operands, f32 accumulate"
         result["components"] = {"gemm_ms": round(mm_ms, 4), "gemm_tflops": round(gemm_tflops, 1),

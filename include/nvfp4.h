@@ -162,6 +162,30 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  * overlap.  Runs on hip_stream and returns after the enqueue. */
 int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream);
 
+/* As nvfp4_gemm, with C quantized in the epilogue instead of stored: the output of one layer leaves
+ * the GEMM as the next layer's NVFP4 activation (the feed-forward chain that the pages' recipe runs
+ * in FP4: hyper.ai (fr) story; aissential.tech article, Method).  out = Q(C), where C is the fp32
+ * matrix nvfp4_gemm would store (c_dtype NVFP4_F32, same operands) and Q quantizes it row-wise in
+ * 1D 16-element blocks along N with nearest-even rounding, exactly as nvfp4_quantize with flags 0,
+ * except that the tensor scale is not derived from C: Q uses *out->tensor_scale, which the caller
+ * writes beforehand (delayed scaling, e.g. from the amax of the previous call: this library's
+ * reading, since the pages do not say how the tensor scale of a GEMM output is chosen).  Elements
+ * beyond 6 times their block scale saturate to +-6 (block scales clamp at 448).
+ * amax: nullable device float; if given, *amax = max(*amax, max |C|) when the GEMM completes (an
+ * atomic maximum, so the caller zeroes it before the first call it should cover); turn it into the
+ * next tensor scale with nvfp4_scale_from_amax.
+ * out: [M x N] descriptor with flags 0, data 16-byte aligned, scales [M][N/16], tensor_scale the
+ * input scale (device).  Supported when K % 128 == 0, K > 0 and both operands' scale arrays are
+ * 8-byte aligned (else NVFP4_ERR_UNSUPPORTED); grouped operands as for nvfp4_gemm.  All buffers are
+ * device memory owned by the caller; out must not overlap the inputs.  Runs on hip_stream. */
+int nvfp4_gemm_nvfp4_out(const nvfp4_tensor *a, const nvfp4_tensor *b, nvfp4_tensor *out, float *amax,
+                         int32_t num_groups, const int64_t *group_row_offsets, void *hip_stream);
+
+/* *ts = RN(*amax / 2688) on the device: the format's FP32 tensor scale for a tensor maximum (amax
+ * maps to 6 * 448, the largest E2M1 value times the largest E4M3 scale; aissential.tech article,
+ * Summary).  amax and ts: device floats, 4-byte aligned.  Runs on hip_stream. */
+int nvfp4_scale_from_amax(const float *amax, float *ts, void *hip_stream);
+
 /* Weight-only 4-bit GEMM, bf16 activations x NVFP4 weights with FP32 accumulation (the W4A16 mode
  * that a serving stack falls back to where the hardware has no FP4 x FP4 product: hyper.ai (de)
  * story on the Nemotron 3 Ultra NVFP4 checkpoint, Hopper):

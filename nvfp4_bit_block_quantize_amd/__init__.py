@@ -24,7 +24,7 @@ __all__ = [
     "NVFP4_ERR_HIP", "NVFP4_F32", "NVFP4_BF16", "NVFP4_COLWISE", "NVFP4_BLOCK2D", "NVFP4_SR",
     "NVFP4_FOUR_OVER_SIX", "NVFP4_TS_FOR_FOUR", "NVFP4_SCALE_SEARCH", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
     "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize",
-    "nvfp4_gemm", "nvfp4_gemm_w4a16", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
+    "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_scale_from_amax", "nvfp4_gemm_w4a16", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
 ]
 
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_HIP = range(6)
@@ -66,6 +66,10 @@ def lib():
         L.nvfp4_dequantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [TP, TP, P, ctypes.c_int, i64, i32, ctypes.POINTER(ctypes.c_int64), P]
         L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_gemm_nvfp4_out.argtypes = [TP, TP, TP, P, i32, ctypes.POINTER(ctypes.c_int64), P]
+        L.nvfp4_gemm_nvfp4_out.restype = ctypes.c_int
+        L.nvfp4_scale_from_amax.argtypes = [P, P, P]
+        L.nvfp4_scale_from_amax.restype = ctypes.c_int
         L.nvfp4_gemm_w4a16.argtypes = [P, ctypes.c_int, i64, i64, TP, P, ctypes.c_int, i64, P]
         L.nvfp4_gemm_w4a16.restype = ctypes.c_int
         L.nvfp4_transpose.argtypes = [TP, TP, P]
@@ -219,6 +223,30 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype: torch.dtype = torch.bf
                           _stream_handle(out.device))
     _check(st, "nvfp4_gemm")
     return out
+
+
+def nvfp4_gemm_nvfp4_out(a: NVFP4Tensor, b: NVFP4Tensor, out: NVFP4Tensor, amax: Optional[torch.Tensor] = None,
+                         group_offsets: Optional[Sequence[int]] = None) -> NVFP4Tensor:
+    """out = Q(A_hat @ B_hat^T), quantized row-wise (1D, nearest-even) in the GEMM's epilogue with the
+    tensor scale already in out.tensor_scale; if amax (float32 [1], device) is given, max |C| is
+    folded into it (see include/nvfp4.h)."""
+    da, db, dout = a.descriptor(), b.descriptor(), out.descriptor()
+    if group_offsets is not None:
+        offs = (ctypes.c_int64 * len(group_offsets))(*[int(v) for v in group_offsets])
+        G = len(group_offsets) - 1
+    else:
+        offs, G = None, 1
+    st = lib().nvfp4_gemm_nvfp4_out(ctypes.byref(da), ctypes.byref(db), ctypes.byref(dout), _ptr(amax), G, offs,
+                                    _stream_handle(out.data.device))
+    _check(st, "nvfp4_gemm_nvfp4_out")
+    return out
+
+
+def nvfp4_scale_from_amax(amax: torch.Tensor, ts: torch.Tensor) -> torch.Tensor:
+    """ts = amax / 2688 on the device (both float32 [1])."""
+    st = lib().nvfp4_scale_from_amax(_ptr(amax), _ptr(ts), _stream_handle(ts.device))
+    _check(st, "nvfp4_scale_from_amax")
+    return ts
 
 
 def nvfp4_gemm_w4a16(a: torch.Tensor, b: NVFP4Tensor, out_dtype: torch.dtype = torch.bfloat16,

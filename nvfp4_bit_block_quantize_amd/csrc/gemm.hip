@@ -54,6 +54,9 @@ struct GemmKArgs {
   int64_t b_group_scales;  // bytes between consecutive groups' B scales
   int32_t group_base;      // index of the first group of this launch (for b offsets)
   int32_t vec_store;       // C and its rows are 16-byte aligned (row-segment stores)
+  uint8_t *q_data, *q_scales;  // quantized output (NVFP4 out only)
+  const float *q_ts;           // its tensor scale (input)
+  float *amax;                 // nullable: max |C| is folded into *amax
   int64_t row_begin[kMaxGroupsPerLaunch + 1];  // A rows of each group
   int32_t tile_begin[kMaxGroupsPerLaunch + 1]; // first tile of each group (prefix sums)
 };
@@ -344,7 +347,8 @@ __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
   return r;
 }
 
-template <bool OUT_BF16, bool A2D, bool B2D>
+// OUT: 0 fp32 C, 1 bf16 C, 2 NVFP4 C (quantized in the epilogue)
+template <int OUT, bool A2D, bool B2D>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kPStage];
   uint8_t *const st0 = smem, *const st1 = smem + kPStage;
@@ -524,7 +528,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
 
   // ---- epilogue
   const float ts = *p.a_ts * p.b_ts[p.group_base + g];
-  store_c_tile<OUT_BF16>(acc, smem, p.c, p.ldc, m0, n0, row_end, p.N, ts, p.vec_store != 0, wave, lane);
+  if constexpr (OUT == 2) {
+    float amax = store_q_tile(acc, smem, p.q_data, p.q_scales, p.N, m0, n0, row_end, ts, *p.q_ts, wave, lane);
+    if (p.amax != nullptr) {
+      // non-negative floats order like their bit patterns: one atomic max per wave
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(p.amax), __float_as_uint(amax));
+    }
+  } else {
+    store_c_tile<OUT == 1>(acc, smem, p.c, p.ldc, m0, n0, row_end, p.N, ts, p.vec_store != 0, wave, lane);
+  }
 }
 
 }  // namespace
@@ -563,7 +577,11 @@ hipError_t launch_gemm(const GemmArgs &a) {
     p.tile_begin[ng] = tiles;
     p.total_tiles = tiles;
     if (tiles == 0) continue;  // K == 0 still launches: the K loop is empty and C = 0
-    const bool bf16 = a.c_dtype == 1;
+    const bool bf16 = a.c_dtype == 1, quant = a.c_dtype == 2;
+    p.q_data = a.q_data;
+    p.q_scales = a.q_scales;
+    p.q_ts = a.q_ts;
+    p.amax = a.amax;
     p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % 16) == 0 && ((a.ldc * (bf16 ? 2 : 4)) % 16) == 0;
     // whole K steps and 8-byte aligned scale rows: branch-free loads
     // (K == 0 takes the generic kernel, whose loads are guarded: the ring's prologue would read the
@@ -575,19 +593,28 @@ hipError_t launch_gemm(const GemmArgs &a) {
     if (full)                                                                                            \
       hipLaunchKernelGGL((gemm_pipe_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p);   \
     else                                                                                                 \
-      hipLaunchKernelGGL((gemm_kernel<OB, A2, B2, false>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
+      hipLaunchKernelGGL((gemm_kernel<OB == 1, A2, B2, false>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
   } while (0)
-    if (bf16) {
-      if (a.a_2d && a.b_2d) NVFP4_GEMM(true, true, true);
-      else if (a.a_2d) NVFP4_GEMM(true, true, false);
-      else if (a.b_2d) NVFP4_GEMM(true, false, true);
-      else NVFP4_GEMM(true, false, false);
+#define NVFP4_GEMM_Q(A2, B2) hipLaunchKernelGGL((gemm_pipe_kernel<2, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
+    if (quant) {
+      // (the entry point admits the quantized output only where the pipelined kernel applies)
+      if (!full) return hipErrorInvalidValue;
+      if (a.a_2d && a.b_2d) NVFP4_GEMM_Q(true, true);
+      else if (a.a_2d) NVFP4_GEMM_Q(true, false);
+      else if (a.b_2d) NVFP4_GEMM_Q(false, true);
+      else NVFP4_GEMM_Q(false, false);
+    } else if (bf16) {
+      if (a.a_2d && a.b_2d) NVFP4_GEMM(1, true, true);
+      else if (a.a_2d) NVFP4_GEMM(1, true, false);
+      else if (a.b_2d) NVFP4_GEMM(1, false, true);
+      else NVFP4_GEMM(1, false, false);
     } else {
-      if (a.a_2d && a.b_2d) NVFP4_GEMM(false, true, true);
-      else if (a.a_2d) NVFP4_GEMM(false, true, false);
-      else if (a.b_2d) NVFP4_GEMM(false, false, true);
-      else NVFP4_GEMM(false, false, false);
+      if (a.a_2d && a.b_2d) NVFP4_GEMM(0, true, true);
+      else if (a.a_2d) NVFP4_GEMM(0, true, false);
+      else if (a.b_2d) NVFP4_GEMM(0, false, true);
+      else NVFP4_GEMM(0, false, false);
     }
+#undef NVFP4_GEMM_Q
 #undef NVFP4_GEMM
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -7,6 +7,8 @@
 
 #include <cstdint>
 
+#include "nvfp4_device.hpp"
+
 namespace nvfp4 {
 namespace gemm {
 
@@ -142,6 +144,63 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
         }
     }
   }
+}
+
+// Quantized epilogue: C = ts_ab * acc (the fp32 values store_c_tile would write) is quantized
+// row-wise in 16-column blocks, nearest-even, with the given tensor scale ts_q: codes to
+// q_data [rows][N / 2], scale bytes to q_scales [rows][N / 16] (N % 16 == 0).  Each wave stages
+// 32 rows x 128 columns of fp32 through LDS (16-byte chunk c of row r at c ^ (r & 31)); lane
+// (row 8 t + (l >> 3), block l & 7) encodes one block per t, so eight lanes write a row's 64 bytes
+// of codes.  Returns the lane's maximum |C| over the blocks it stored.
+__device__ __forceinline__ float store_q_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *q_data, uint8_t *q_scales,
+                                              int64_t N, int64_t m0, int64_t n0, int64_t row_end, float ts_ab,
+                                              float ts_q, uint32_t wave, uint32_t lane) {
+  const uint32_t h = lane >> 5, l32 = lane & 31u;
+  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  // all waves are done with the stages and the last (re-fetch) loads have landed
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  lds_barrier();
+  constexpr uint32_t ROWB = 512;  // 128 fp32
+  uint8_t *const region = smem + wave * (32 * ROWB);
+  const int64_t qrow = N / 2, srow = N / 16;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ch = 8 * j + 2 * q + h;
+        *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & 31)) * 16) =
+            make_float4(acc[j][i][4 * q] * ts_ab, acc[j][i][4 * q + 1] * ts_ab, acc[j][i][4 * q + 2] * ts_ab,
+                        acc[j][i][4 * q + 3] * ts_ab);
+      }
+    // the wave reads back its own rows (LDS accesses of one wave complete in order)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t row = 8 * t + (lane >> 3), blk = lane & 7u;
+      float y[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4 *>(region + row * ROWB + (((4 * blk + u) ^ (row & 31)) * 16));
+        y[4 * u] = v.x;
+        y[4 * u + 1] = v.y;
+        y[4 * u + 2] = v.z;
+        y[4 * u + 3] = v.w;
+      }
+      const int64_t grow = m0 + wm + 32 * i + row, gcol = n0 + wn + 16 * blk;
+      if (grow < row_end && gcol < N) {
+        const float ab = block_absmax(y);
+        amax = fmaxf(amax, ab);
+        uint32_t sbyte, w0, w1;
+        encode_block_rne(y, ab, ts_q, sbyte, w0, w1);
+        *reinterpret_cast<uint2 *>(q_data + grow * qrow + gcol / 2) = make_uint2(w0, w1);
+        q_scales[grow * srow + gcol / 16] = static_cast<uint8_t>(sbyte);
+      }
+    }
+  }
+  return amax;
 }
 
 }  // namespace gemm

@@ -153,16 +153,17 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int y_dtype, int64_t ldy, 
   return status_of(nvfp4::launch_dequantize(a));
 }
 
-int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, int32_t num_groups,
-               const int64_t *group_row_offsets, void *hip_stream) {
+namespace {
+
+// Shared validation of the NVFP4 x NVFP4 GEMM entry points (shapes, groups, operand pointers).
+int validate_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups, const int64_t *group_row_offsets) {
   if (!a || !b) return NVFP4_ERR_NULL;
-  if (dtype_size(c_dtype) == 0) return NVFP4_ERR_UNSUPPORTED;
   if (num_groups < 0 || (num_groups > 1 && !group_row_offsets)) return NVFP4_ERR_SHAPE;
   const int64_t M = a->rows, N = b->rows, K = a->k;
-  if (M < 0 || N < 0 || K < 0 || b->k != K || K % 16 != 0 || ldc < N || ldc < 1) return NVFP4_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || b->k != K || K % 16 != 0) return NVFP4_ERR_SHAPE;
   if ((a->flags & NVFP4_BLOCK2D) && M % 16 != 0) return NVFP4_ERR_SHAPE;
   if ((b->flags & NVFP4_BLOCK2D) && N % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (M * K >= kMaxIndex || N * K >= kMaxIndex || M * ldc >= kMaxIndex * 4) return NVFP4_ERR_SHAPE;
+  if (M * K >= kMaxIndex || N * K >= kMaxIndex) return NVFP4_ERR_SHAPE;
   if (num_groups > 1 || group_row_offsets) {
     const int32_t G = num_groups < 1 ? 1 : num_groups;
     if (group_row_offsets[0] != 0 || group_row_offsets[G] != M) return NVFP4_ERR_SHAPE;
@@ -170,12 +171,16 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
       if (group_row_offsets[g + 1] < group_row_offsets[g]) return NVFP4_ERR_SHAPE;
   }
   if (M == 0 || N == 0) return NVFP4_OK;
-  if (!a->tensor_scale || !b->tensor_scale || !c) return NVFP4_ERR_NULL;
-  if (K > 0) {  // (with K == 0 no code or scale is read and C = 0)
+  if (!a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
+  if (K > 0) {  // (with K == 0 no code or scale is read)
     if (!a->data || !a->scales || !b->data || !b->scales) return NVFP4_ERR_NULL;
     if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
   }
-  if ((reinterpret_cast<uintptr_t>(c) & static_cast<uintptr_t>(dtype_size(c_dtype) - 1)) != 0) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4::GemmArgs gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups,
+                          const int64_t *group_row_offsets, void *hip_stream) {
   nvfp4::GemmArgs g{};
   g.a_data = a->data;
   g.a_scales = a->scales;
@@ -185,16 +190,65 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
   g.b_scales = b->scales;
   g.b_ts = b->tensor_scale;
   g.b_2d = (b->flags & NVFP4_BLOCK2D) != 0;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.c = c;
-  g.c_dtype = c_dtype == NVFP4_BF16 ? 1 : 0;
-  g.ldc = ldc;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->k;
   g.num_groups = num_groups < 1 ? 1 : num_groups;
   g.group_offsets = group_row_offsets;
   g.stream = static_cast<hipStream_t>(hip_stream);
+  return g;
+}
+
+}  // namespace
+
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, int32_t num_groups,
+               const int64_t *group_row_offsets, void *hip_stream) {
+  if (!a || !b) return NVFP4_ERR_NULL;
+  if (dtype_size(c_dtype) == 0) return NVFP4_ERR_UNSUPPORTED;
+  int st = validate_gemm(a, b, num_groups, group_row_offsets);
+  if (st != NVFP4_OK) return st;
+  const int64_t M = a->rows, N = b->rows;
+  if (ldc < N || ldc < 1 || M * ldc >= kMaxIndex * 4) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!c) return NVFP4_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(c) & static_cast<uintptr_t>(dtype_size(c_dtype) - 1)) != 0) return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g = gemm_args(a, b, num_groups, group_row_offsets, hip_stream);
+  g.c = c;
+  g.c_dtype = c_dtype == NVFP4_BF16 ? 1 : 0;
+  g.ldc = ldc;
   return status_of(nvfp4::launch_gemm(g));
+}
+
+int nvfp4_gemm_nvfp4_out(const nvfp4_tensor *a, const nvfp4_tensor *b, nvfp4_tensor *out, float *amax,
+                         int32_t num_groups, const int64_t *group_row_offsets, void *hip_stream) {
+  if (!a || !b || !out) return NVFP4_ERR_NULL;
+  int st = validate_gemm(a, b, num_groups, group_row_offsets);
+  if (st != NVFP4_OK) return st;
+  const int64_t M = a->rows, N = b->rows, K = a->k;
+  if (out->rows != M || out->k != N) return NVFP4_ERR_SHAPE;
+  if (out->flags != 0) return NVFP4_ERR_UNSUPPORTED;  // row-wise 1D blocks, nearest-even only
+  if (M == 0 || N == 0) return NVFP4_OK;
+  // the quantized epilogue lives in the pipelined kernel: whole 128-element K steps, 8-byte
+  // aligned scale rows
+  if (K == 0 || K % 128 != 0 || (reinterpret_cast<uintptr_t>(a->scales) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(b->scales) & 7u) != 0)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (!out->data || !out->scales || !out->tensor_scale) return NVFP4_ERR_NULL;
+  if (!aligned16(out->data) || (amax && (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)) return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g = gemm_args(a, b, num_groups, group_row_offsets, hip_stream);
+  g.c_dtype = 2;
+  g.ldc = N;
+  g.q_data = out->data;
+  g.q_scales = out->scales;
+  g.q_ts = out->tensor_scale;
+  g.amax = amax;
+  return status_of(nvfp4::launch_gemm(g));
+}
+
+int nvfp4_scale_from_amax(const float *amax, float *ts, void *hip_stream) {
+  if (!amax || !ts) return NVFP4_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(amax) & 3u) != 0 || (reinterpret_cast<uintptr_t>(ts) & 3u) != 0) return NVFP4_ERR_ALIGN;
+  return status_of(nvfp4::launch_scale_from_amax(amax, ts, static_cast<hipStream_t>(hip_stream)));
 }
 
 int nvfp4_gemm_w4a16(const void *a, int a_dtype, int64_t m, int64_t lda, const nvfp4_tensor *b, void *c,

@@ -65,6 +65,52 @@ __device__ __forceinline__ uint32_t e2m1_rne_index(float v) {
   return vc < 1.0f ? small : big;
 }
 
+// ---- nearest-even block encode (shared by the quantize passes and the GEMM's quantized epilogue) ------
+__device__ __forceinline__ uint32_t sign_code(float y) { return (__float_as_uint(y) >> 28) & 8u; }
+
+// e == +inf (S * ts underflowed): nonzero elements saturate to 6, zeros stay zero.
+__device__ __forceinline__ uint32_t code_degenerate(float y) {
+  return (y == 0.0f ? 0u : 7u) | sign_code(y);
+}
+
+// Nearest-even codes of 8 values times e, packed (code n at bits 4n).  The hardware conversion
+// (scale 1.0) rounds to nearest-even and saturates at 6.
+__device__ __forceinline__ uint32_t pack8_rne(const float *y, float e) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * e, y[1] * e, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * e, y[3] * e, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * e, y[5] * e, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * e, y[7] * e, 1.0f, 3);
+  return w;
+}
+
+__device__ __forceinline__ float block_absmax(const float (&y)[16]) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) ab = fmaxf(ab, fabsf(y[t]));
+  return ab;
+}
+
+// One 1D block, nearest-even: scale byte and the two packed code words.
+__device__ __forceinline__ void encode_block_rne(const float (&y)[16], float ab, float ts, uint32_t &sbyte,
+                                                 uint32_t &w0, uint32_t &w1) {
+  float S;
+  sbyte = block_scale(ab, 6.0f, ts, S);
+  const float e = encode_factor(S, ts);
+  if (__builtin_isinf(e)) {
+    w0 = 0u;
+    w1 = 0u;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      w0 |= code_degenerate(y[t]) << (4 * t);
+      w1 |= code_degenerate(y[8 + t]) << (4 * t);
+    }
+  } else {
+    w0 = pack8_rne(y, e);
+    w1 = pack8_rne(y + 8, e);
+  }
+}
+
 // Stochastic rounding of v >= 0 with 16 random bits r16: between the grid neighbours lo <= v < hi
 // round up iff r16 < f * 65536, f = (v - lo) / (hi - lo) (exact); v >= 6 gives 6.  Both sub-ranges
 // are evaluated and selected (no divergent branches): below 1 the step is 0.5; from 1 up, lo is v with

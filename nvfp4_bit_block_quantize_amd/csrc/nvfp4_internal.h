@@ -54,6 +54,10 @@ struct GemmArgs {
   int32_t num_groups;
   const int64_t *group_offsets;  // host, num_groups + 1 (nullptr for a plain GEMM)
   hipStream_t stream;
+  // c_dtype 2: C quantized to NVFP4 (1D, nearest-even) with tensor scale *q_ts; amax nullable
+  uint8_t *q_data = nullptr, *q_scales = nullptr;
+  const float *q_ts = nullptr;
+  float *amax = nullptr;
 };
 
 struct W4A16Args {
@@ -84,6 +88,7 @@ hipError_t launch_dequantize(const DequantArgs &a);
 hipError_t launch_gemm(const GemmArgs &a);
 hipError_t launch_transpose(const TransposeLaunch &a);
 hipError_t launch_gemm_w4a16(const W4A16Args &a);
+hipError_t launch_scale_from_amax(const float *amax, float *ts, hipStream_t stream);
 
 // Host copy of the Philox4x32-10 block function (for the RHT sign word).
 void philox4x32_10_host(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);

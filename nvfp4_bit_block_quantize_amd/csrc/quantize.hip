@@ -97,25 +97,8 @@ __device__ __forceinline__ float raw8_elem(const Raw8<ESZ> &r, int c) {
 }
 
 // ---- element codes --------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t sign_code(float y) { return (__float_as_uint(y) >> 28) & 8u; }
-
 __device__ __forceinline__ uint32_t code_sr(float y, float e, uint32_t r16) {
   return e2m1_sr_index(fabsf(y) * e, r16) | sign_code(y);
-}
-
-// e == +inf (S * ts underflowed): nonzero elements saturate to 6, zeros stay zero.
-__device__ __forceinline__ uint32_t code_degenerate(float y) {
-  return (y == 0.0f ? 0u : 7u) | sign_code(y);
-}
-
-// Nearest-even codes of 8 values times e, packed (code n at bits 4n).
-__device__ __forceinline__ uint32_t pack8_rne(const float *y, float e) {
-  uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * e, y[1] * e, 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * e, y[3] * e, 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * e, y[5] * e, 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * e, y[7] * e, 1.0f, 3);
-  return w;
 }
 
 // Decode a code under scale S: RN(RN(q * S) * ts).
@@ -200,13 +183,6 @@ __device__ __forceinline__ void encode_block(const float (&y)[16], float ab, flo
       }
     }
   }
-}
-
-__device__ __forceinline__ float block_absmax(const float (&y)[16]) {
-  float ab = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) ab = fmaxf(ab, fabsf(y[t]));
-  return ab;
 }
 
 // Workgroup max of one value per lane -> partial[blockIdx.x] (thread 0).  NT = threads per group.
@@ -801,6 +777,18 @@ hipError_t launch_quantize(const QuantArgs &a) {
     return hipGetLastError();
   }
   return a.dtype == 1 ? dispatch_quantize<2>(a) : dispatch_quantize<4>(a);
+}
+
+namespace {
+// The format's tensor scale for a tensor maximum: ts = RN(amax / 2688), as pass 1 computes it.
+__global__ void scale_from_amax_kernel(const float *amax, float *ts) {
+  if (threadIdx.x == 0) *ts = *amax / 2688.0f;
+}
+}  // namespace
+
+hipError_t launch_scale_from_amax(const float *amax, float *ts, hipStream_t stream) {
+  hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(64), 0, stream, amax, ts);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

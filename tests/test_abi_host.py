@@ -157,3 +157,26 @@ def test_gemm_w4a16_validation():
     assert g(c=FAKE + 1) == nv.NVFP4_ERR_ALIGN
     assert g(m=0) == nv.NVFP4_OK                                 # empty: no-op
     assert g(b_=_desc(0, 128)) == nv.NVFP4_OK
+
+
+def test_gemm_nvfp4_out_validation():
+    L = nv.lib()
+    a, b = _desc(64, 256), _desc(32, 256)
+    q = lambda a_=a, b_=b, o=None, amax=FAKE, G=1, offs=None: L.nvfp4_gemm_nvfp4_out(
+        ctypes.byref(a_) if a_ else None, ctypes.byref(b_) if b_ else None,
+        ctypes.byref(o if o is not None else _desc(64, 32)) if o is not False else None, amax, G, offs, None)
+    assert q(o=False) == nv.NVFP4_ERR_NULL
+    assert q(a_=None) == nv.NVFP4_ERR_NULL
+    assert q(o=_desc(64, 48)) == nv.NVFP4_ERR_SHAPE                      # out must be [M x N]
+    assert q(o=_desc(64, 32, nv.NVFP4_BLOCK2D)) == nv.NVFP4_ERR_UNSUPPORTED  # row-wise 1D only
+    assert q(o=_desc(64, 32, nv.NVFP4_SR)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert q(a_=_desc(64, 192), b_=_desc(32, 192)) == nv.NVFP4_ERR_UNSUPPORTED  # K % 128
+    assert q(a_=_desc(64, 256, scales=FAKE + 4)) == nv.NVFP4_ERR_UNSUPPORTED   # scale rows 8-byte aligned
+    assert q(o=_desc(64, 32, data=0)) == nv.NVFP4_ERR_NULL
+    assert q(o=_desc(64, 32, ts=0)) == nv.NVFP4_ERR_NULL
+    assert q(o=_desc(64, 32, data=MIS)) == nv.NVFP4_ERR_ALIGN
+    assert q(amax=FAKE + 2) == nv.NVFP4_ERR_ALIGN
+    assert q(G=2) == nv.NVFP4_ERR_SHAPE                                   # groups without offsets
+    assert q(a_=_desc(0, 256), o=_desc(0, 32)) == nv.NVFP4_OK            # empty: no-op
+    assert L.nvfp4_scale_from_amax(None, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert L.nvfp4_scale_from_amax(FAKE, FAKE + 2, None) == nv.NVFP4_ERR_ALIGN
