@@ -7,7 +7,8 @@ window) is checked against the oracle's double-precision product of the GPU's ow
 
 405B-shaped FFN forward (X [8192 x 16384] ~N(0,1) with 0.1% outlier channels x20, W [53248 x
 16384] ~N(0,0.01) with 16x16 scaling): both quantizations checked bit-exactly in full, and 64
-seeded 128 x 128 tiles of Y = X W^T (bf16 out) against the oracle.
+seeded 128 x 128 tiles of Y = X W^T (bf16 out) against the oracle; then the W4A16 GEMM of 16 and
+40 tokens against the same weight (2D and 1D scales), 48 seeded column windows each.
 """
 import os
 
@@ -93,7 +94,8 @@ def test_fprop405b_quantize_full_and_gemm_tiles(oracle):
     assert_quant_equal(qx, oracle.quantize(oracle_input(x)), "405B X 1D")
     print("[405b] oracle quantize W", flush=True)
     assert_quant_equal(qw, oracle.quantize(oracle_input(w), flags=nv.NVFP4_BLOCK2D), "405B W 2D")
-    del x, w
+    x_dec = x[:40].clone()  # decode-sized activation batches for the W4A16 checks below
+    del x
     M, N, K = qx.rows, qw.rows, qx.k
     worst = 0.0
     for (r0, c0, h, wd) in seeded_tiles(M, N, 64, seed=5):
@@ -103,3 +105,22 @@ def test_fprop405b_quantize_full_and_gemm_tiles(oracle):
         got = y[r0:r0 + h, c0:c0 + wd].float().cpu().numpy()
         worst = max(worst, gemm_check(got, cref, bnd, True, f"405B tile ({r0},{c0})"))
     print(f"[405b] 64 tiles of 8192x53248x16384: max |err|/bound {worst:.2e}", flush=True)
+
+    # W4A16 at the same weight size: 16 tokens against the 2D-quantized W (weight streaming, one
+    # M tile), 40 tokens against W quantized with 1D blocks (three M tiles); 48 seeded windows of
+    # 128 output columns each against the oracle
+    windows = [(0, c0, 1, 128) for (_, c0, _, _) in seeded_tiles(1, N, 48, seed=6)]
+    for rows, flags in ((16, nv.NVFP4_BLOCK2D), (40, 0)):
+        qw_w = qw if flags else nv.nvfp4_quantize(w.cuda())
+        a16 = x_dec[:rows].to(torch.bfloat16)
+        yw = nv.nvfp4_gemm_w4a16(a16.cuda(), qw_w, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        a_bits = synth.bf16_bits(a16)
+        worst = 0.0
+        for (_, c0, _, wd) in windows:
+            b_t = _host_rows(qw_w, c0, c0 + wd, block2d=bool(flags))
+            cref, bnd = oracle.gemm_w4a16_ref(a_bits, b_t, rows, wd, K)
+            worst = max(worst, gemm_check(yw[:, c0:c0 + wd].cpu().numpy(), cref, bnd, False,
+                                          f"405B W4A16 {rows} rows flags={flags} cols {c0}"))
+        print(f"[405b] W4A16 {rows}x53248x16384 (flags {flags}), 48 windows: max |err|/bound {worst:.2e}", flush=True)
+        del qw_w
