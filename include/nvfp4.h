@@ -175,8 +175,8 @@ int nvfp4_transpose(const nvfp4_tensor *in, nvfp4_tensor *out, void *hip_stream)
  * atomic maximum, so the caller zeroes it before the first call it should cover); turn it into the
  * next tensor scale with nvfp4_scale_from_amax.
  * out: [M x N] descriptor with flags 0, data 16-byte aligned, scales [M][N/16], tensor_scale the
- * input scale (device).  Supported when K % 128 == 0, K > 0 and both operands' scale arrays are
- * 8-byte aligned (else NVFP4_ERR_UNSUPPORTED); grouped operands as for nvfp4_gemm.  All buffers are
+ * input scale (device).  Supported when K % 256 == 0, K > 0 and both operands' scale arrays are
+ * 16-byte aligned (else NVFP4_ERR_UNSUPPORTED); grouped operands as for nvfp4_gemm.  All buffers are
  * device memory owned by the caller; out must not overlap the inputs.  Runs on hip_stream. */
 int nvfp4_gemm_nvfp4_out(const nvfp4_tensor *a, const nvfp4_tensor *b, nvfp4_tensor *out, float *amax,
                          int32_t num_groups, const int64_t *group_row_offsets, void *hip_stream);

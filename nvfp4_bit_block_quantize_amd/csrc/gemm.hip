@@ -327,8 +327,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmKArgs p) {
 // consecutive columns of one row of C (staged through LDS for whole-row-segment stores).
 // Rows beyond the operand read a clamped valid row: their products reach only outputs that are never
 // stored.  Steps beyond K re-fetch the last step into a stage that is never consumed.
-constexpr int kPA = 0, kPB = 16384, kPSA = 32768, kPSB = 34816, kPStage = 36864;  // stage layout (bytes)
-constexpr int kLoadsPerStage = 12;  // direct loads issued per lane per stage
+// PAIRED (an even number of K steps, 16-byte aligned scale rows): block scales travel two K steps
+// at a time.  A row's 16 scale bytes of steps 2P and 2P + 1 are contiguous in memory, so one 16-byte
+// direct load per lane moves 64 rows' worth.  They live in a ring of three slots of their own (A
+// [256 rows][16 B], then B); pair P is loaded during steps 2P - 4 (A) and 2P - 3 (B), one load per
+// wave each, so every step issues the same nine loads per lane (eight for codes) and the waits are
+// constants.  Pair P's slot is reused for pair P + 3, first written in step 2P + 2, after the barrier
+// of step 2P + 1 that follows the last read of pair P.
+// Otherwise each stage carries its step's scales ([256 rows][8 B] per operand, dword loads: waves
+// 0-1 A's, 2-3 B's), twelve loads per lane per step.
+constexpr int kPA = 0, kPB = 16384, kPCodes = 32768;  // code stage layout (bytes)
+constexpr int kPSlot = 8192;                          // PAIRED: one scale slot, A then B, 4 KB each
+constexpr int kPSA = 32768, kPSB = 34816;             // otherwise: the stage's scales
+template <bool PAIRED>
+struct PipeLayout {
+  static constexpr int kStage = PAIRED ? kPCodes : kPCodes + 4096;
+  static constexpr int kScales = 3 * kStage;  // PAIRED: the three scale slots follow the stages
+  static constexpr int kBytes = 3 * kStage + (PAIRED ? 3 * kPSlot : 0);
+  static constexpr int kLoadsPerStage = PAIRED ? 9 : 12;  // direct loads issued per lane per step
+};
 
 // Chunk c (16 B) of tile row r is stored at position c ^ swz(r) of its 64-byte row: 8 or 16
 // consecutive rows reading the same chunk touch distinct 16-byte bank groups of a 128- or 256-byte
@@ -348,10 +365,13 @@ __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
 }
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 NVFP4 C (quantized in the epilogue)
-template <int OUT, bool A2D, bool B2D>
+template <int OUT, bool A2D, bool B2D, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kPStage];
+  using L = PipeLayout<PAIRED>;
+  constexpr int kPStage = L::kStage, kLoadsPerStage = L::kLoadsPerStage;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::kBytes];
   uint8_t *const st0 = smem, *const st1 = smem + kPStage;
+  uint8_t *const slots = smem + L::kScales;
 
   const int32_t tile = xcd_tile(blockIdx.x, p.total_tiles);
   int32_t g = 0;
@@ -365,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
   const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
-  const int64_t KT = p.K / 128;
+  const int64_t KT = p.K / 128, KP = KT / 2;  // K steps, pairs of steps
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -374,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
 
   // ---- direct-load sources: 32-bit per-lane offsets (an operand is below 2 GiB) from per-step bases
   const int64_t row_bytes = p.K / 2, KB = p.K / 16;
-  uint32_t srcA[4], srcB[4], srcS[4];
+  uint32_t srcA[4], srcB[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t R = 64 * wave + 16 * i + (lane >> 2);  // tile row this lane fetches
@@ -383,7 +403,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
     srcA[i] = static_cast<uint32_t>(ra * row_bytes + 16 * c);
     srcB[i] = static_cast<uint32_t>(rb * row_bytes + 16 * c);
   }
-  // scales [256 rows][8 B] per operand: waves 0-1 stage A's, waves 2-3 B's, 64 dwords per load
+  // PAIRED scale pairs: wave w fetches rows [64 w, 64 w + 64) of A's (even steps) or B's (odd steps)
+  // slot.  Otherwise [256 rows][8 B] per operand per step: waves 0-1 stage A's, waves 2-3 B's, 64
+  // dwords per load.
+  uint32_t srcSA, srcSB, srcS[4];
+  {
+    const int64_t ra = min(m0 + 64 * wave + lane, row_end - 1), rb = min(n0 + 64 * wave + lane, p.N - 1);
+    srcSA = static_cast<uint32_t>(A2D ? (ra / 16) * KB : ra * KB);
+    srcSB = static_cast<uint32_t>(B2D ? (rb / 16) * KB : rb * KB);
+  }
   const bool is_a = wave < 2;
   const uint8_t *sc_base = is_a ? p.a_scales : b_scales;
   {
@@ -395,24 +423,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
       srcS[i] = static_cast<uint32_t>((two_d ? (r / 16) * KB : r * KB) + 4 * (lane & 1));
     }
   }
-  const uint32_t lds_codes = 4096 * wave;                                    // + 1024 i
-  const uint32_t lds_sc = (is_a ? kPSA : kPSB) + 1024 * (wave & 1);         // + 256 i
-  auto issue = [&](uint8_t *st, int64_t kt) {
+  const uint32_t lds_codes = 4096 * wave;                             // + 1024 i
+  const uint32_t lds_sc = (is_a ? kPSA : kPSB) + 1024 * (wave & 1);  // + 256 i (not PAIRED)
+  auto issue_codes = [&](uint8_t *st, int64_t kt) {
     const int64_t kc = kt < KT ? kt : KT - 1;
-    const uint8_t *ga = p.a_data + kc * 64, *gb = b_data + kc * 64, *gs = sc_base + kc * 8;
+    const uint8_t *ga = p.a_data + kc * 64, *gb = b_data + kc * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lds_load16(ga + srcA[i], st + kPA + lds_codes + 1024 * i);
       lds_load16(gb + srcB[i], st + kPB + lds_codes + 1024 * i);
     }
+    if constexpr (!PAIRED) {
+      const uint8_t *gs = sc_base + kc * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
+      for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
+    }
   };
+  // PAIRED, half 0: A's scales of pair pp, half 1: B's; pairs past K re-fetch the last pair
+  auto issue_scales = [&](uint8_t *slot, int64_t pp, int half) {
+    const int64_t pc = pp < KP ? pp : KP - 1;
+    if (half == 0) lds_load16(p.a_scales + pc * 16 + srcSA, slot + 1024 * wave);
+    else lds_load16(b_scales + pc * 16 + srcSB, slot + 4096 + 1024 * wave);
+  };
+  auto slot_of = [&](int64_t pp) { return slots + kPSlot * static_cast<uint32_t>(pp % 3); };
 
   // ---- fragment reads: lane half h takes codes [64 h, 64 h + 64) of the step, chunk q of its half
   const uint32_t rdA = (wm + l32) * 64, rdB = (wn + l32) * 64;
   const uint32_t pos0 = 16 * ((2 * h) ^ swz(l32)), pos1 = 16 * ((2 * h + 1) ^ swz(l32));
-  const uint32_t rsA = kPSA + (wm + l32) * 8 + 4 * h, rsB = kPSB + (wn + l32) * 8 + 4 * h;
+  const uint32_t rsA = PAIRED ? (wm + l32) * 16 + 4 * h : kPSA + (wm + l32) * 8 + 4 * h;
+  const uint32_t rsB = PAIRED ? 4096 + (wn + l32) * 16 + 4 * h : kPSB + (wn + l32) * 8 + 4 * h;
   auto read_chunk = [&](const uint8_t *st, uint32_t pos, uint4 (&ca)[4], uint4 (&cb)[4]) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -420,11 +459,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
       cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + rdB + 2048 * f + pos);
     }
   };
-  auto read_scales = [&](const uint8_t *st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+  // the scale words of step kt (blocks 4 h .. 4 h + 3): out of its pair's slot, or its stage
+  auto read_scales = [&](const uint8_t *src, int64_t kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+    const uint32_t par = PAIRED ? 8 * static_cast<uint32_t>(kt & 1) : 0u;
+    constexpr uint32_t kFrag = PAIRED ? 512 : 256;  // 32 rows
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      sa[f] = *reinterpret_cast<const uint32_t *>(st + rsA + 256 * f);
-      sb[f] = *reinterpret_cast<const uint32_t *>(st + rsB + 256 * f);
+      sa[f] = *reinterpret_cast<const uint32_t *>(src + rsA + par + kFrag * f);
+      sb[f] = *reinterpret_cast<const uint32_t *>(src + rsB + par + kFrag * f);
     }
   };
 
@@ -436,17 +478,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  // ---- prologue: steps 0 and 1 in flight, step 0's first chunk read and its sub-step 0 decoded
-  issue(st0, 0);
-  issue(st1, 1);
-  wait_vmcnt<kLoadsPerStage>();
+  // ---- prologue: steps 0 and 1 and scale pairs 0 and 1 in flight, step 0's first chunk read and
+  // its sub-step 0 decoded
+  if constexpr (PAIRED) {
+    issue_scales(slots, 0, 0);
+    issue_scales(slots, 0, 1);
+  }
+  issue_codes(st0, 0);
+  if constexpr (PAIRED) {
+    issue_scales(slots + kPSlot, 1, 0);
+    issue_scales(slots + kPSlot, 1, 1);
+  }
+  issue_codes(st1, 1);
+  wait_vmcnt<PAIRED ? 10 : kLoadsPerStage>();  // step 1 (and pair 1) may still be in flight
   lds_barrier();
   uint4 ca0[4], cb0[4], ca1[4], cb1[4];  // chunk 0 / chunk 1 codes of the current step
   uint4 psa[4], psb[4];                   // fp16 scale pairs of the current step (blocks 4h..4h+3)
   {
     uint32_t rsa[4], rsb[4];
     read_chunk(st0, pos0, ca0, cb0);
-    read_scales(st0, rsa, rsb);
+    read_scales(PAIRED ? slots : st0, 0, rsa, rsb);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       psa[f] = scale_pairs4(rsa[f]);
@@ -460,9 +511,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
     bfc[f] = decode8(cb0[f].x, psb[f].x);
   }
 
-  // one K step out of stage S: the 8 sub-steps of 16 codes, 16 MFMAs each
-  auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt, int64_t kt) {
-    issue(tgt, kt + 2);
+  // one K step out of stage cur: the 8 sub-steps of 16 codes, 16 MFMAs each.  sc_nxt holds the next
+  // step's scale pair, sc_tgt receives half of a later pair (distinct slots).
+  auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt,
+                  const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int64_t kt) {
+    issue_codes(tgt, kt + 2);
+    if constexpr (PAIRED) issue_scales(sc_tgt, (kt + 4) >> 1, static_cast<int>(kt & 1));
     read_chunk(cur, pos1, ca1, cb1);
     uint32_t nsa[4], nsb[4];  // next step's raw scale bytes
 #pragma unroll
@@ -513,13 +567,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
         wait_lgkmcnt0();
         lds_barrier();
         read_chunk(nxt, pos0, ca0, cb0);
-        read_scales(nxt, nsa, nsb);
+        read_scales(PAIRED ? sc_nxt : nxt, kt + 1, nsa, nsb);
       }
     }
   };
   uint8_t *cur = st0, *nxt = st1, *tgt = smem + 2 * kPStage;
   for (int64_t kt = 0; kt < KT; ++kt) {
-    step(cur, nxt, tgt, kt);
+    if constexpr (PAIRED) step(cur, nxt, tgt, slot_of((kt + 1) >> 1), slot_of((kt + 4) >> 1), kt);
+    else step(cur, nxt, tgt, nullptr, nullptr, kt);
     uint8_t *const done = cur;
     cur = nxt;
     nxt = tgt;
@@ -583,22 +638,27 @@ hipError_t launch_gemm(const GemmArgs &a) {
     p.q_ts = a.q_ts;
     p.amax = a.amax;
     p.vec_store = (reinterpret_cast<uintptr_t>(a.c) % 16) == 0 && ((a.ldc * (bf16 ? 2 : 4)) % 16) == 0;
-    // whole K steps and 8-byte aligned scale rows: branch-free loads
-    // (K == 0 takes the generic kernel, whose loads are guarded: the ring's prologue would read the
-    // clamped step -1)
+    // whole K steps and 8-byte aligned scale rows: branch-free loads (K == 0 takes the generic
+    // kernel, whose loads are guarded: the ring's prologue would read the clamped step -1); whole
+    // pairs of steps and 16-byte aligned scale rows (K % 256 == 0 makes every row a multiple of 16
+    // bytes): scales two steps per load
     const bool full = a.K > 0 && (a.K % 128) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0;
+    const bool paired = full && (a.K % 256) == 0 && (reinterpret_cast<uintptr_t>(a.a_scales) & 15u) == 0 &&
+                        (reinterpret_cast<uintptr_t>(a.b_scales) & 15u) == 0;
 #define NVFP4_GEMM(OB, A2, B2)                                                                            \
   do {                                                                                                   \
-    if (full)                                                                                            \
-      hipLaunchKernelGGL((gemm_pipe_kernel<OB, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p);   \
+    if (paired)                                                                                          \
+      hipLaunchKernelGGL((gemm_pipe_kernel<OB, A2, B2, true>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
+    else if (full)                                                                                       \
+      hipLaunchKernelGGL((gemm_pipe_kernel<OB, A2, B2, false>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
     else                                                                                                 \
       hipLaunchKernelGGL((gemm_kernel<OB == 1, A2, B2, false>), dim3(tiles), dim3(kThreads), 0, a.stream, p); \
   } while (0)
-#define NVFP4_GEMM_Q(A2, B2) hipLaunchKernelGGL((gemm_pipe_kernel<2, A2, B2>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
+#define NVFP4_GEMM_Q(A2, B2) hipLaunchKernelGGL((gemm_pipe_kernel<2, A2, B2, true>), dim3(tiles), dim3(kThreads), 0, a.stream, p)
     if (quant) {
-      // (the entry point admits the quantized output only where the pipelined kernel applies)
-      if (!full) return hipErrorInvalidValue;
+      // (the entry point admits the quantized output only where the paired pipelined kernel applies)
+      if (!paired) return hipErrorInvalidValue;
       if (a.a_2d && a.b_2d) NVFP4_GEMM_Q(true, true);
       else if (a.a_2d) NVFP4_GEMM_Q(true, false);
       else if (a.b_2d) NVFP4_GEMM_Q(false, true);

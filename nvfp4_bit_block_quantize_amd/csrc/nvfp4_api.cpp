@@ -228,10 +228,10 @@ int nvfp4_gemm_nvfp4_out(const nvfp4_tensor *a, const nvfp4_tensor *b, nvfp4_ten
   if (out->rows != M || out->k != N) return NVFP4_ERR_SHAPE;
   if (out->flags != 0) return NVFP4_ERR_UNSUPPORTED;  // row-wise 1D blocks, nearest-even only
   if (M == 0 || N == 0) return NVFP4_OK;
-  // the quantized epilogue lives in the pipelined kernel: whole 128-element K steps, 8-byte
-  // aligned scale rows
-  if (K == 0 || K % 128 != 0 || (reinterpret_cast<uintptr_t>(a->scales) & 7u) != 0 ||
-      (reinterpret_cast<uintptr_t>(b->scales) & 7u) != 0)
+  // the quantized epilogue lives in the pipelined kernel: whole pairs of 128-element K steps,
+  // 16-byte aligned scale arrays
+  if (K == 0 || K % 256 != 0 || (reinterpret_cast<uintptr_t>(a->scales) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(b->scales) & 15u) != 0)
     return NVFP4_ERR_UNSUPPORTED;
   if (!out->data || !out->scales || !out->tensor_scale) return NVFP4_ERR_NULL;
   if (!aligned16(out->data) || (amax && (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)) return NVFP4_ERR_ALIGN;

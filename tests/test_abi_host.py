@@ -170,8 +170,9 @@ def test_gemm_nvfp4_out_validation():
     assert q(o=_desc(64, 48)) == nv.NVFP4_ERR_SHAPE                      # out must be [M x N]
     assert q(o=_desc(64, 32, nv.NVFP4_BLOCK2D)) == nv.NVFP4_ERR_UNSUPPORTED  # row-wise 1D only
     assert q(o=_desc(64, 32, nv.NVFP4_SR)) == nv.NVFP4_ERR_UNSUPPORTED
-    assert q(a_=_desc(64, 192), b_=_desc(32, 192)) == nv.NVFP4_ERR_UNSUPPORTED  # K % 128
-    assert q(a_=_desc(64, 256, scales=FAKE + 4)) == nv.NVFP4_ERR_UNSUPPORTED   # scale rows 8-byte aligned
+    assert q(a_=_desc(64, 192), b_=_desc(32, 192)) == nv.NVFP4_ERR_UNSUPPORTED  # K % 256
+    assert q(a_=_desc(64, 384), b_=_desc(32, 384), o=_desc(64, 32)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert q(a_=_desc(64, 256, scales=FAKE + 8)) == nv.NVFP4_ERR_UNSUPPORTED   # scales 16-byte aligned
     assert q(o=_desc(64, 32, data=0)) == nv.NVFP4_ERR_NULL
     assert q(o=_desc(64, 32, ts=0)) == nv.NVFP4_ERR_NULL
     assert q(o=_desc(64, 32, data=MIS)) == nv.NVFP4_ERR_ALIGN

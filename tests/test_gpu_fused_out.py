@@ -50,8 +50,8 @@ def _operands(M, N, K, seed, b_flags=0):
     return nv.nvfp4_quantize(a.cuda()), nv.nvfp4_quantize(w.cuda(), flags=b_flags)
 
 
-@pytest.mark.parametrize("M,N,K,b_flags", [(200, 272, 256, 2), (256, 256, 1024, 0), (1, 16, 128, 0),
-                                           (513, 528, 384, 2)])
+@pytest.mark.parametrize("M,N,K,b_flags", [(200, 272, 256, 2), (256, 256, 1024, 0), (1, 16, 256, 0),
+                                           (513, 528, 768, 2)])
 def test_fused_out_matches_oracle_quantization_of_fp32_c(oracle, M, N, K, b_flags):
     print(f"[fused] {M}x{N}x{K} b_flags={b_flags}", flush=True)
     qa, qb = _operands(M, N, K, 11, b_flags)
@@ -86,7 +86,7 @@ def test_fused_out_ideal_scale_equals_plain_quantize(oracle):
 
 
 def test_fused_out_amax_is_a_running_maximum():
-    qa, qb = _operands(64, 64, 128, 13)
+    qa, qb = _operands(64, 64, 256, 13)
     c32 = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32)
     big = float(c32.abs().max()) * 3
     amax = torch.full((1,), big, dtype=torch.float32, device="cuda")

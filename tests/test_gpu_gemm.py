@@ -53,6 +53,17 @@ def test_gemm_ragged_shapes(oracle, M, N, K, out_dtype):
     _gemm_case(oracle, a, b, out_dtype=out_dtype, what=f"{M}x{N}x{K}")
 
 
+# the pipelined kernel moves block scales two K steps at a time: K = 256 (one pair, later pairs
+# clamped), 768 (three pairs), 1280; K = 384 (an odd number of steps) takes the guarded kernel
+@pytest.mark.parametrize("K", [256, 384, 768, 1280])
+@pytest.mark.parametrize("flags", [(0, 0), (2, 2), (0, 2)])
+def test_gemm_k_pairs(oracle, K, flags):
+    a = synth.normal((272, K), 1.0, seed=9, tensor_id=70, dtype=torch.bfloat16)
+    b = synth.normal((528, K), 0.05, seed=9, tensor_id=71, dtype=torch.bfloat16)
+    _gemm_case(oracle, a, b, a_flags=flags[0], b_flags=flags[1], out_dtype=torch.float32,
+               what=f"K={K} flags={flags}")
+
+
 def test_gemm_2d_weight_scales(oracle):
     a = synth.normal((96, 512), 1.0, seed=2, tensor_id=62)
     b = synth.normal((160, 512), 0.02, seed=2, tensor_id=63)
