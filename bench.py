@@ -101,7 +101,7 @@ def traffic_summary(d):
     gw, nw = _counter_per_dispatch(os.path.join(d, "pmc_WRITE_SIZE", "p_counter_collection.csv"), "gemm", "WRITE_SIZE")
     fs, ws = copy_kib / cf, copy_kib / cw
     M, N, K = 8192, 14336, 4096
-    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/{d} -o p -- python3 $REPO/bench.py {a}"
+    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $OUT/{d} -o p -- python3 $REPO/bench.py {a}"
     out = {
         "what": "HBM-side traffic per launch of the NVFP4 GEMM (fprop 8192x14336x4096, bf16 out), from rocprofv3 "
                 "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the dispatches), each scaled by the "
@@ -110,7 +110,7 @@ def traffic_summary(d):
                      cmd.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", a="--steps 2 --warmup 1 --no-cpu"),
                      cmd.format(c="FETCH_SIZE", d="cpy_FETCH_SIZE", a="--copy-calibration 1024"),
                      cmd.format(c="WRITE_SIZE", d="cpy_WRITE_SIZE", a="--copy-calibration 1024"),
-                     "python3 bench.py --traffic-summary gpurun_out"],
+                     "python3 bench.py --traffic-summary $OUT"],
         "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1), "copy_true_kib_each_way": copy_kib,
         "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
         "gemm_dispatches": [nf, nw],
