@@ -287,6 +287,25 @@ def main():
         unfused_ms = per_call_ms(unfused)
     qa_ms = per_call_ms(q_a) if not w4a16 else 0.0
     qb_ms = per_call_ms(q_b) if not w4a16 else 0.0
+
+    # the same calls with the input out of the caches: back-to-back calls re-read a tensor that fits
+    # the 256 MB Infinity Cache from there; here 1 GiB is read before each call (a read, so no dirty
+    # lines are written back inside the timed call) and each call is timed alone between two events
+    def cold_ms(fn, reps=5):
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        total = 0.0
+        for _ in range(reps):
+            flush.max()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            total += e0.elapsed_time(e1)
+        del flush
+        return total / reps
+    qa_cold = cold_ms(q_a) if qbytes else 0.0
+    qb_cold = cold_ms(q_b) if qbytes else 0.0
     mm_ms = per_call_ms(mm)
     step()
     torch.cuda.synchronize()
@@ -343,6 +362,9 @@ def main():
         "components": {
             "quantize_gbps": round(quant_gbps, 1),
             "quantize_hbm_frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
+            "quantize_cold_gbps": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9, 1) if qbytes else None,
+            "quantize_cold_a_ms": round(qa_cold, 4),
+            "quantize_cold_b_ms": round(qb_cold, 4),
             "quantize_a_ms": round(qa_ms, 4),
             "quantize_b_ms": round(qb_ms, 4),
             "quantize_algorithmic_bytes": qbytes,
