@@ -306,6 +306,13 @@ def main():
         return total / reps
     qa_cold = cold_ms(q_a) if qbytes else 0.0
     qb_cold = cold_ms(q_b) if qbytes else 0.0
+
+    # copy ceiling: a device-to-device copy of the bf16 X (read + write, the same buffer sizes as the
+    # quantize inputs), back to back like the quantize calls
+    copy_dst = torch.empty_like(x)
+    copy_ms = per_call_ms(lambda: copy_dst.copy_(x))
+    copy_gbps = 2 * x.numel() * x.element_size() / (copy_ms * 1e-3) / 1e9
+    del copy_dst
     mm_ms = per_call_ms(mm)
     step()
     torch.cuda.synchronize()
@@ -363,6 +370,8 @@ def main():
             "quantize_gbps": round(quant_gbps, 1),
             "quantize_hbm_frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
             "quantize_cold_gbps": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9, 1) if qbytes else None,
+            "copy_ceiling_gbps": round(copy_gbps, 1),
+            "quantize_frac_of_copy": round(quant_gbps / copy_gbps, 4) if qbytes else None,
             "quantize_cold_a_ms": round(qa_cold, 4),
             "quantize_cold_b_ms": round(qb_cold, 4),
             "quantize_a_ms": round(qa_ms, 4),
@@ -423,6 +432,23 @@ def cpu_baseline(a, nv):
     t2 = time.perf_counter()
     flops = 2.0 * rows * rows * K
     qbytes = quant_bytes(rows, K, False) + quant_bytes(rows, K, True)
+    # one core, on an eighth of the sample
+    r1 = max(16, rows // 8)
+    s0 = time.perf_counter()
+    qx1 = oracle.quantize(xs[:r1], nthreads=1)
+    qw1 = oracle.quantize(wsmp[:r1], flags=oracle.BLOCK2D, nthreads=1)
+    s1 = time.perf_counter()
+    oracle.gemm_ref(qx1, qw1, r1, r1, K, nthreads=1)
+    s2 = time.perf_counter()
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(flops / (t2 - t0) / 1e12, 6),
         "unit": "TFLOP/s",
@@ -432,6 +458,11 @@ def cpu_baseline(a, nv):
         "seconds": round(t2 - t0, 3),
         "quantize_gbps": round(qbytes / (t1 - t0) / 1e9, 3),
         "gemm_gflops": round(flops / (t2 - t1) / 1e9, 3),
+        "one_core": {"sample": f"quantize X[:{r1}], W[:{r1}], GEMM {r1}x{r1}x{K}",
+                     "quantize_gbps": round((quant_bytes(r1, K, False) + quant_bytes(r1, K, True)) / (s1 - s0) / 1e9, 3),
+                     "gemm_gflops": round(2.0 * r1 * r1 * K / (s2 - s1) / 1e9, 3)},
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model,
     }
 
 
