@@ -79,8 +79,9 @@ __device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_
 // 8 (r >> 2) + 4 h + (r & 3).  Whole tiles go through LDS (smem, at least 4 x 32 x 512 bytes, no
 // longer read by any wave's pending loads), 32 rows of the wave's quarter at a time, so that each
 // store writes 16 consecutive bytes per lane and four (bf16) or two (fp32) complete 256 / 512-byte
-// row segments per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row).
-// Partial tiles, or C without 16-byte aligned rows, take element stores.
+// row segments per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row);
+// rows at or beyond row_end are not written.  Tiles cut by N, or C without 16-byte aligned rows,
+// take element stores.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts,
@@ -88,7 +89,7 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  if (vec_store && m0 + BM <= row_end && n0 + BN <= N) {
+  if (vec_store && n0 + BN <= N) {
     // all waves are done with the stages and the last (re-fetch) loads have landed
     wait_vmcnt<0>();
     wait_lgkmcnt0();
@@ -96,8 +97,10 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
     constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
     uint8_t *const region = smem + wave * (32 * ROWB);
     uint8_t *const gbase = c + ((m0 + wm) * ldc + n0 + wn) * ES;
+    const int64_t rows_left = row_end - (m0 + wm);  // rows of the wave's quarter that exist
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (32 * i >= rows_left) break;  // wave-uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -121,7 +124,7 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
       for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
         const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
         const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
-        *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * ldc * ES + u * 16) = v;
+        if (32 * i + row < rows_left) *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * ldc * ES + u * 16) = v;
       }
     }
   } else {

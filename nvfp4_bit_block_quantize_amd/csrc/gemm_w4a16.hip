@@ -95,14 +95,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(W4Args p) {
   if (KT > 0) {
     // ---- direct-load sources (32-bit offsets from per-step bases; each operand is below 4 GiB).
     // Wave w fetches tile rows [64 w, 64 w + 64) of A (8 rows per load), of the B codes (32 rows
-    // per load) and of the B scales (one dword per row).  Rows beyond the operand read a clamped
-    // valid row: their products reach only outputs that are never stored.
+    // per load) and of the B scales (one dword per row).  Rows beyond the operand read some valid
+    // row: their products reach only outputs that are never stored.
     uint32_t srcA[8], srcB[2], srcS;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t R = 64 * wave + 8 * i + (lane >> 3);
       const uint32_t c = (lane & 7u) ^ swz_a(R);  // logical chunk stored at position lane & 7
-      srcA[i] = static_cast<uint32_t>(min(m0 + R, p.M - 1) * p.lda_bytes + 16 * c);
+      // rows beyond M read a valid row chosen modulo M (not all the last row: many lanes on one
+      // address are slow)
+      const int64_t ra = m0 + R < p.M ? m0 + R : (m0 + R) % p.M;
+      srcA[i] = static_cast<uint32_t>(ra * p.lda_bytes + 16 * c);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(W4Args p) {
 
 // ---- few activation rows (decode): weight streaming --------------------------------------------------
 // With M <= 64 the product is bound by reading the weight once from HBM.  A workgroup of W waves owns
-// 64 weight rows (four 16-row tiles) and all M <= 16 MT activation rows; its waves split K, wave w
+// 64 weight rows (four 16-row tiles) and 16 MT activation rows (all of them for M <= 64; for M up
+// to 192 the grid's second dimension walks 64-row chunks, each a pass over the weight, the later
+// ones mostly from the Infinity Cache); its waves split K, wave w
 // taking the 128-element chunks w, w + W, ... (neighbouring waves read neighbouring bytes of each row),
 // and their partial sums meet in LDS at the end.
 // Per chunk and lane (n = l & 15, g = l >> 4):
@@ -291,6 +296,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) 
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t n16 = lane & 15u, g = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kSkRows;
+  const uint32_t m_base = 16 * MT * blockIdx.y;  // this workgroup's activation rows
   const int64_t KC = p.K / 128, KB = p.K / 16, row_bytes = p.K / 2;
 
   // per-lane sources: 32-bit byte offsets of chunk 0 (each operand is below 4 GiB)
@@ -301,9 +307,18 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) 
     srcB[nt] = static_cast<uint32_t>(n * row_bytes + 16 * g);
     srcS[nt] = static_cast<uint32_t>(B2D ? (n / 16) * KB : n * KB);
   }
-  // activation rows 16 mt + 4 t + (l >> 4), clamped to the last row (their sums are never stored)
-  const uint32_t a_last = static_cast<uint32_t>(p.M - 1), a_r0 = lane >> 4, a_piece = 16 * (lane & 15);
+  // activation rows m_base + 16 mt + 4 t + (l >> 4); rows beyond M read a valid row chosen modulo M
+  // (their sums are never stored)
+  const uint32_t a_rows = static_cast<uint32_t>(p.M), a_r0 = lane >> 4, a_piece = 16 * (lane & 15);
   const uint32_t lda_b = static_cast<uint32_t>(p.lda_bytes);
+  uint32_t a_off[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t r = m_base + 16 * mt + 4 * t + a_r0;
+      a_off[mt][t] = (r < a_rows ? r : r % a_rows) * lda_b + a_piece;
+    }
   // v_perm selector picking scale bytes 2 t + (g >> 1), t = 0..3, out of the chunk's eight
   const uint32_t sh = g >> 1;
   const uint32_t ssel = sh | ((2 + sh) << 8) | ((4 + sh) << 16) | ((6 + sh) << 24);
@@ -330,8 +345,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        ch.a[mt][t] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, min(16 * mt + 4 * t + a_r0, a_last) * lda_b + a_piece + oa, 0, 0));
+        ch.a[mt][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[mt][t] + oa, 0, 0));
   };
   // activation chunk -> this wave's LDS buffer -> MFMA fragments (see above)
   uint8_t *const tr = a_tr[wave];
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) 
 #pragma unroll
     for (int h = 0; h < 16 / W; ++h) {
       const uint32_t mr = r0 + W * h;  // row within the M tile
-      const int64_t m = 16 * mt + mr;
+      const int64_t m = m_base + 16 * mt + mr;
       const uint32_t off = (mt * 4 + nt) * kSkRed + 64 * (mr & 3) + (col & 15) + 16 * (mr >> 2);
       float v = 0.0f;
 #pragma unroll
@@ -445,7 +459,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_w4a16_skinny_kernel(SkArgs p) 
 template <int MT>
 void launch_skinny(const W4A16Args &a, const SkArgs &p) {
   constexpr int W = 4, R = 2;
-  const dim3 grid(static_cast<uint32_t>((a.N + kSkRows - 1) / kSkRows)), block(64 * W);
+  const dim3 grid(static_cast<uint32_t>((a.N + kSkRows - 1) / kSkRows),
+                  static_cast<uint32_t>((a.M + 16 * MT - 1) / (16 * MT))),
+      block(64 * W);
   if (a.c_dtype == 1) {
     if (a.b_2d) hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, true, true>), grid, block, 0, a.stream, p);
     else hipLaunchKernelGGL((gemm_w4a16_skinny_kernel<MT, W, R, true, false>), grid, block, 0, a.stream, p);
@@ -458,8 +474,10 @@ void launch_skinny(const W4A16Args &a, const SkArgs &p) {
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const W4A16Args &a) {
-  // few activation rows, whole 128-element chunks, 8-byte aligned scale rows: weight streaming
-  if (a.M > 0 && a.M <= 64 && a.N > 0 && a.K > 0 && a.K % 128 == 0 &&
+  // few activation rows, whole 128-element chunks, 8-byte aligned scale rows: weight streaming,
+  // one pass over the weight per 64 activation rows (up to 192 rows: beyond, the tiled kernel's
+  // single pass over the weight wins)
+  if (a.M > 0 && a.M <= 192 && a.N > 0 && a.K > 0 && a.K % 128 == 0 &&
       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0 && (a.M - 1) * a.lda * 2 + 2 * a.K < (int64_t(1) << 31)) {
     SkArgs p{};
     p.a = static_cast<const uint8_t *>(a.a);
@@ -472,7 +490,7 @@ hipError_t launch_gemm_w4a16(const W4A16Args &a) {
     p.K = a.K;
     p.c = static_cast<uint8_t *>(a.c);
     p.ldc = a.ldc;
-    switch ((a.M + 15) / 16) {
+    switch (a.M <= 64 ? (a.M + 15) / 16 : 4) {
       case 1: launch_skinny<1>(a, p); break;
       case 2: launch_skinny<2>(a, p); break;
       case 3: launch_skinny<3>(a, p); break;
