@@ -12,7 +12,13 @@ the codes and scales written) and the GEMM-only TFLOP/s; `roofline` describes th
 (the GEMM) against the MI355X dense fp16 MFMA peak; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload fprop8b|wgrad8b] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu]
+
+Other workloads (--workload): fprop8b_q (the GEMM output quantized in the epilogue), dgrad8b,
+wgrad8b (RHT + stochastic rounding), w4a16_8b and w4a16_decode (bf16 activations x NVFP4 weights),
+fprop405b (the Llama-3.1-405B FFN forward, 8192x53248x16384) and moe (64 experts [4096x1536],
+Zipf(1.1) top-2 loads over 16384 tokens, grouped GEMM).  The CPU oracle baseline is timed on the
+default workload only.
 """
 import argparse
 import json
@@ -34,7 +40,8 @@ def _args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop8b",
-                   choices=["fprop8b", "fprop8b_q", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode"])
+                   choices=["fprop8b", "fprop8b_q", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode",
+                            "fprop405b", "moe"])
     p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
@@ -154,6 +161,9 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return
 
+    if a.workload == "moe":
+        run_moe(a, nv, torch, synth, dev)
+        return
     if a.workload in ("fprop8b", "fprop8b_q"):
         x_cpu, w_cpu = synth.fprop8b(0)
         M, K = x_cpu.shape
@@ -164,6 +174,14 @@ def main():
         if a.workload == "fprop8b_q":
             workload = ("Llama-3-8B FFN fprop: X[8192x4096] bf16 1D blocks, W[14336x4096] bf16 16x16 tiles, "
                         "Y quantized to NVFP4 (1D) in the GEMM epilogue, tensor scale from the previous step's amax")
+        qbytes = quant_bytes(M, K, False) + quant_bytes(N, K, True)
+    elif a.workload == "fprop405b":
+        x_cpu, w_cpu = synth.fprop405b(0)
+        M, K = x_cpu.shape
+        N = w_cpu.shape[0]
+        fa, fb, rht = 0, nv.NVFP4_BLOCK2D, False
+        out_dtype = torch.bfloat16
+        workload = "Llama-3.1-405B FFN fprop: X[8192x16384] bf16 1D blocks, W[53248x16384] bf16 16x16 tiles, Y bf16"
         qbytes = quant_bytes(M, K, False) + quant_bytes(N, K, True)
     elif a.workload == "dgrad8b":
         dy_cpu, _ = synth.wgrad8b(0)
@@ -406,8 +424,158 @@ def main():
             gbps = w4_bytes / (mm_ms * 1e-3) / 1e9
             result["roofline"].update({"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                                        "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)})
-    if not a.no_cpu and not w4a16:
+    if not a.no_cpu and a.workload == "fprop8b":
         result["cpu_baseline"] = cpu_baseline(a, nv)
+    print(json.dumps(result), flush=True)
+
+
+def run_moe(a, nv, torch, synth, dev):
+    """MoE expert layer, one step: nvfp4_quantize of the routed activations X_sorted [32768 x 4096]
+    (rows already in expert order: the token gather / dispatch happens before the step),
+    nvfp4_quantize_grouped of the 64 expert weights W_e [4096 x 1536] (column-wise, so blocks run
+    along K = 4096, with Four-over-Six, each expert its own tensor scale) into one group-contiguous
+    B, then the grouped GEMM Y_e = X_e W_e^T, bf16 out.  For comparison the experts are also
+    quantized by 64 separate nvfp4_quantize calls (captured as one graph)."""
+    import numpy as np
+    E, K, N, T = 64, 4096, 1536, 16384
+    experts = synth.moe_experts(0, E, K, N, workers=max(1, min(16, os.cpu_count() or 1)))
+    w_all = torch.stack(experts).to(dev)  # [E, K, N]
+    del experts
+    tokens = synth.moe_tokens(0, T, K)
+    loads, slot_token = synth.moe_routing(T, E, 2, 1.1, 0)
+    offs = [int(v) for v in np.concatenate([[0], np.cumsum(loads)])]
+    M = offs[-1]
+    xg = tokens[torch.from_numpy(slot_token)].to(dev)  # [32768, 4096]
+    del tokens
+    fl = nv.NVFP4_COLWISE | nv.NVFP4_FOUR_OVER_SIX
+    qa = nv.empty_like_quantized(M, K, 0, dev)
+    qb = nv.NVFP4Tensor(torch.empty((E * N, K // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((E * N, K // 16), dtype=torch.uint8, device=dev),
+                        torch.empty(E, dtype=torch.float32, device=dev), N, K, fl, E)
+    views = [nv.NVFP4Tensor(qb.data[e * N:(e + 1) * N], qb.scales[e * N:(e + 1) * N],
+                            qb.tensor_scale[e:e + 1], N, K, fl) for e in range(E)]
+    ws_a = torch.empty(nv.nvfp4_workspace_size(M, K, 0) // 4, dtype=torch.int32, device=dev)
+    ws_b = torch.empty(nv.nvfp4_workspace_size(K, N, fl) // 4, dtype=torch.int32, device=dev)
+    ws_bg = torch.empty(E * nv.nvfp4_workspace_size(K, N, fl) // 4, dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def q_a():
+        nv.nvfp4_quantize(xg, out=qa, workspace=ws_a)
+
+    def q_b():
+        nv.nvfp4_quantize_grouped(w_all, flags=fl, out=qb, workspace=ws_bg)
+
+    def q_b_separate():
+        for e in range(E):
+            nv.nvfp4_quantize(w_all[e], flags=fl, out=views[e], workspace=ws_b)
+
+    def mm():
+        nv.nvfp4_gemm(qa, qb, out=y, group_offsets=offs)
+
+    def step():
+        q_a(); q_b(); mm()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def per_call_ms(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        mm()
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    qa_ms, qb_ms, mm_ms = per_call_ms(q_a), per_call_ms(q_b), per_call_ms(mm)
+    step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(y, y_eager):
+        print(json.dumps({"error": "graph replay differs from eager result"}))
+        sys.exit(1)
+    # the experts as 64 separate calls, as one graph: 128 short kernels, launch gaps included
+    g_b = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_b):
+        q_b_separate()
+    for _ in range(a.warmup):
+        graph.replay()
+        g_b.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        g_b.replay()
+    e1.record()
+    e1.synchronize()
+    qb_graph_ms = e0.elapsed_time(e1) / a.steps
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (mm_ms * 1e-3) / 1e12
+    qa_bytes = quant_bytes(M, K, False)
+    qb_bytes = E * quant_bytes(N, K, False)
+    tiles = int(sum((int(m) + 255) // 256 for m in loads)) * (N // 256)
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 x e4m3) -> exact f16 operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "MoE experts: 64 x W_e[4096x1536] Student-t(4) col-wise 4/6, X_sorted[32768x4096] "
+                               "(16384 tokens, top-2, Zipf(1.1) loads) 1D, grouped Y_e = X_e W_e^T bf16",
+                   "M": M, "N": N, "K": K, "groups": E, "out": "bfloat16",
+                   "loads_min_max": [int(loads.min()), int(loads.max())]},
+        "components": {
+            "quantize_x_ms": round(qa_ms, 4),
+            "quantize_x_gbps": round(qa_bytes / (qa_ms * 1e-3) / 1e9, 1),
+            "quantize_experts_ms": round(qb_ms, 4),
+            "quantize_experts_gbps": round(qb_bytes / (qb_ms * 1e-3) / 1e9, 1),
+            "quantize_experts_frac_hbm": round(qb_bytes / (qb_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "quantize_experts_separate_calls_graph_ms": round(qb_graph_ms, 4),
+            "quantize_algorithmic_bytes": qa_bytes + qb_bytes,
+            "gemm_ms": round(mm_ms, 4),
+            "gemm_tflops": round(gemm_tflops, 1),
+            "gemm_tiles": tiles,
+            "gemm_tile_fill": round(M * N / (tiles * 256 * 256), 4),
+            "step_timing": "HIP graph replay of quantize(X_sorted) + grouped quantize(64 W_e) + grouped GEMM; "
+                           "components: mean of back-to-back launches",
+        },
+        "roofline": {
+            "kernel": "nvfp4 grouped gemm",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -102,8 +102,9 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, uint32_t flags);
 /* Quantize x [rows x cols] (dtype NVFP4_F32 or NVFP4_BF16, leading dimension ldx elements) to
  * NVFP4.  Two kernels run on the stream: the tensor amax pass, then the block-scale / encode /
  * pack pass (which also writes *out->tensor_scale).
- * flags: any of NVFP4_COLWISE, NVFP4_BLOCK2D, NVFP4_SR, NVFP4_FOUR_OVER_SIX, except the
- *   unsupported combinations SR|FOUR_OVER_SIX, SR|BLOCK2D and FOUR_OVER_SIX|BLOCK2D.
+ * flags: any of NVFP4_COLWISE, NVFP4_BLOCK2D, NVFP4_SR, NVFP4_FOUR_OVER_SIX, NVFP4_TS_FOR_FOUR,
+ *   NVFP4_SCALE_SEARCH, except SR with FOUR_OVER_SIX, SCALE_SEARCH or BLOCK2D, and SCALE_SEARCH
+ *   with FOUR_OVER_SIX or BLOCK2D (NVFP4_ERR_UNSUPPORTED).
  * Logical matrix: Y = x (R = rows, K = cols), or Y = x^T with NVFP4_COLWISE (R = cols, K = rows).
  *   K % 16 == 0; with NVFP4_BLOCK2D also R % 16 == 0; with NVFP4_COLWISE also cols % 8 == 0.
  * out: caller-filled descriptor with rows == R, k == K, (flags & NVFP4_BLOCK2D) equal to the
@@ -127,6 +128,21 @@ int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
 int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                        uint32_t flags, uint64_t seed, uint32_t stream_id, uint64_t sign_seed,
                        float *rht_out, nvfp4_tensor *out, void *workspace, void *hip_stream);
+
+/* Grouped quantize (MoE expert weights, each with its own tensor scale; the routed experts are the
+ * NVFP4 part of the hyper.ai (de) story's Nemotron 3 Ultra checkpoint): `groups` equally shaped tensors
+ * x_g = x + g * group_stride elements (g = 0 .. groups-1, each [rows x cols] with leading dimension
+ * ldx), quantized in one pair of launches.  Group g is exactly nvfp4_quantize(x_g, x_dtype, rows,
+ * cols, ldx, flags, seed, stream_id + g, out_g, ...), where out_g is group g of out: out->rows == R
+ * and out->k == K per group as for nvfp4_quantize, and out->data / out->scales / out->tensor_scale
+ * hold `groups` consecutive tensors (R*K/2 and R*K/16 or R*K/256 bytes, one float each), the layout
+ * of a grouped nvfp4_gemm weight.  Flags and shape rules as nvfp4_quantize.
+ * groups: 1 .. 65535 and group_stride >= 0 elements with (groups - 1) * group_stride <= 2^36 (else
+ * NVFP4_ERR_SHAPE); group_stride * sizeof(dtype) a multiple of 16 (else NVFP4_ERR_ALIGN).  workspace: device, groups * nvfp4_workspace_size() bytes,
+ * 16-byte aligned.  All buffers are device memory owned by the caller; out must not overlap x. */
+int nvfp4_quantize_grouped(const void *x, int x_dtype, int64_t groups, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t group_stride, uint32_t flags, uint64_t seed, uint32_t stream_id,
+                           nvfp4_tensor *out, void *workspace, void *hip_stream);
 
 /* Decode an NVFP4 tensor to y [in->rows x in->k] (dtype NVFP4_F32 or NVFP4_BF16, leading
  * dimension ldy elements): y = RN(RN(q * S) * ts), rounded once more to bf16 (nearest-even) for a

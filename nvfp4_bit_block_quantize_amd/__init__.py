@@ -62,6 +62,8 @@ def lib():
         L.nvfp4_quantize.restype = ctypes.c_int
         L.nvfp4_rht_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, u32, u64, u32, u64, P, TP, P, P]
         L.nvfp4_rht_quantize.restype = ctypes.c_int
+        L.nvfp4_quantize_grouped.argtypes = [P, ctypes.c_int, i64, i64, i64, i64, i64, u32, u64, u32, TP, P, P]
+        L.nvfp4_quantize_grouped.restype = ctypes.c_int
         L.nvfp4_dequantize.argtypes = [TP, P, ctypes.c_int, i64, P]
         L.nvfp4_dequantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [TP, TP, P, ctypes.c_int, i64, i32, ctypes.POINTER(ctypes.c_int64), P]
@@ -175,6 +177,30 @@ def nvfp4_quantize(x: torch.Tensor, flags: int = 0, seed: int = 0, stream_id: in
     st = lib().nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), x.shape[0], x.shape[1], _ld(x), flags, seed & (2**64 - 1),
                               stream_id, ctypes.byref(desc), _ptr(workspace), _stream_handle(x.device))
     _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_quantize_grouped(x: torch.Tensor, flags: int = 0, seed: int = 0, stream_id: int = 0,
+                           out: Optional[NVFP4Tensor] = None, workspace: Optional[torch.Tensor] = None) -> NVFP4Tensor:
+    """Quantize each x[g] of x (float32 / bfloat16 [groups x rows x cols], each x[g] with unit column
+    stride) with its own tensor scale, group g with stream id stream_id + g, into one group-contiguous
+    NVFP4 tensor (the grouped GEMM's weight layout; see include/nvfp4.h)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [groups, rows, cols]")
+    G, rows, cols = x.shape
+    if G < 1:
+        raise ValueError("x needs at least one group")
+    R, K = _logical(x[0], flags)
+    if out is None:
+        out = empty_like_quantized(R, K, flags, x.device, groups=G)
+    if workspace is None:
+        workspace = torch.empty(G * nvfp4_workspace_size(rows, cols, flags) // 4, dtype=torch.int32, device=x.device)
+    desc = out.descriptor()
+    ldx = _ld(x[0])
+    st = lib().nvfp4_quantize_grouped(_ptr(x), _dtype_code(x.dtype), G, rows, cols, ldx, x.stride(0) if G > 1 else 0,
+                                      flags, seed & (2**64 - 1), stream_id, ctypes.byref(desc), _ptr(workspace),
+                                      _stream_handle(x.device))
+    _check(st, "nvfp4_quantize_grouped")
     return out
 
 

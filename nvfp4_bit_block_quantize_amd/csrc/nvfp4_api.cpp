@@ -12,6 +12,7 @@ namespace {
 constexpr uint32_t kKnownFlags =
     NVFP4_COLWISE | NVFP4_BLOCK2D | NVFP4_SR | NVFP4_FOUR_OVER_SIX | NVFP4_TS_FOR_FOUR | NVFP4_SCALE_SEARCH;
 constexpr int64_t kMaxIndex = int64_t(1) << 32;  // element / chunk counts are 32-bit in the kernels
+constexpr int64_t kMaxQuantGroups = 65535;        // groups run along the grid's y dimension
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -57,12 +58,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 
 int run_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
                  uint64_t seed, uint32_t stream_id, bool rht, uint64_t sign_seed, float *rht_out,
-                 nvfp4_tensor *out, void *workspace, void *hip_stream) {
+                 nvfp4_tensor *out, void *workspace, void *hip_stream, int64_t groups = 1, int64_t group_stride = 0) {
   int64_t R = 0, K = 0;
   int st = validate_quantize(x, x_dtype, rows, cols, ldx, flags, rht, out, workspace, &R, &K);
   if (st != NVFP4_OK) return st;
   if (rht_out && !aligned16(rht_out)) return NVFP4_ERR_ALIGN;
   nvfp4::QuantArgs a{};
+  a.groups = groups;
+  a.x_group_bytes = group_stride * dtype_size(x_dtype);
   a.x = x;
   a.dtype = x_dtype == NVFP4_BF16 ? 1 : 0;
   a.rows = rows;
@@ -135,6 +138,17 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
                        void *workspace, void *hip_stream) {
   return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, true, sign_seed, rht_out, out, workspace,
                       hip_stream);
+}
+
+int nvfp4_quantize_grouped(const void *x, int x_dtype, int64_t groups, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t group_stride, uint32_t flags, uint64_t seed, uint32_t stream_id,
+                           nvfp4_tensor *out, void *workspace, void *hip_stream) {
+  if (groups < 1 || groups > kMaxQuantGroups) return NVFP4_ERR_SHAPE;
+  if (group_stride < 0 || (groups > 1 && group_stride > (kMaxIndex << 4) / (groups - 1))) return NVFP4_ERR_SHAPE;
+  const int es = dtype_size(x_dtype);
+  if (es != 0 && (group_stride * es) % 16 != 0) return NVFP4_ERR_ALIGN;
+  return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, false, 0, nullptr, out, workspace,
+                      hip_stream, groups, group_stride);
 }
 
 int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int y_dtype, int64_t ldy, void *hip_stream) {

@@ -26,6 +26,8 @@ struct QuantArgs {
   float *ts;
   uint32_t *workspace;
   hipStream_t stream;
+  int64_t groups = 1;         // equally shaped tensors quantized by one call (grid dimension y)
+  int64_t x_group_bytes = 0;  // bytes between consecutive groups' inputs
 };
 
 struct DequantArgs {

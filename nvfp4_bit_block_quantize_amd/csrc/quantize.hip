@@ -101,13 +101,18 @@ __device__ __forceinline__ uint32_t code_sr(float y, float e, uint32_t r16) {
   return e2m1_sr_index(fabsf(y) * e, r16) | sign_code(y);
 }
 
-// Decode a code under scale S: RN(RN(q * S) * ts).
-__device__ __forceinline__ float decode(uint32_t code, float S, float ts) {
-  uint32_t idx = code & 7u;
-  uint32_t qb = idx >= 2u ? (idx + 252u) << 22 : (idx == 1u ? 0x3F000000u : 0u);
-  float q = __uint_as_float(qb | ((code & 8u) << 28));
-  float p = q * S;
-  return p * ts;
+// Decoded error terms of one byte of packed codes (two elements, low nibble first) under scale S:
+// the decoded value is RN(RN(q * S) * ts), where q * S is exact (q has at most two significant bits,
+// S four, and the product stays normal).  v_cvt_scalef32_pk_f32_fp4 with scale 1.0 returns the two
+// E2M1 values q exactly, so each element costs half a conversion and two multiplies.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int BYTE>
+__device__ __forceinline__ float sse_pair(uint32_t w, float y0, float y1, float S, float ts, float acc) {
+  const f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BYTE);
+  const float d0 = y0 - (q[0] * S) * ts;
+  acc = fmaf(d0, d0, acc);
+  const float d1 = y1 - (q[1] * S) * ts;
+  return fmaf(d1, d1, acc);
 }
 
 // Packed codes of one 16-element block under factor e.  i0 = logical index of y[0] (a multiple of
@@ -145,13 +150,14 @@ __device__ __forceinline__ void block_words(const float (&y)[16], float e, uint6
 // fp32 squared error of a block against its decoded codes, accumulated with fma in block order.
 __device__ __forceinline__ float block_sse(const float (&y)[16], uint32_t w0, uint32_t w1, float S, float ts) {
   float acc = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const uint32_t code = ((t < 8 ? w0 : w1) >> (4 * (t & 7))) & 15u;
-    const float diff = y[t] - decode(code, S, ts);
-    acc = fmaf(diff, diff, acc);
-  }
-  return acc;
+  acc = sse_pair<0>(w0, y[0], y[1], S, ts, acc);
+  acc = sse_pair<1>(w0, y[2], y[3], S, ts, acc);
+  acc = sse_pair<2>(w0, y[4], y[5], S, ts, acc);
+  acc = sse_pair<3>(w0, y[6], y[7], S, ts, acc);
+  acc = sse_pair<0>(w1, y[8], y[9], S, ts, acc);
+  acc = sse_pair<1>(w1, y[10], y[11], S, ts, acc);
+  acc = sse_pair<2>(w1, y[12], y[13], S, ts, acc);
+  return sse_pair<3>(w1, y[14], y[15], S, ts, acc);
 }
 
 // Full encode of one 1D block: scale byte and two packed words (nibble t at bits 4t).  With
@@ -215,6 +221,26 @@ __device__ __forceinline__ float tensor_scale(const uint32_t *__restrict__ parti
   return ts;
 }
 
+// ---- groups ------------------------------------------------------------------------------------------
+// A grouped call (grid dimension y = group g) quantizes G equally shaped tensors in one launch per
+// pass: group g reads x + g * x bytes, writes its codes and scale bytes at g times the per-group
+// sizes and its tensor scale to ts_out[g], keeps its pass-1 maxima at partial + g * (pass-1
+// workgroups), and draws its stochastic rounding from stream stream_id + g.  That is exactly what a
+// separate call on the group's tensor with stream id stream_id + g computes.
+struct GroupStrides {
+  int64_t x, data, scales;  // bytes per group
+};
+
+template <class A>
+__device__ __forceinline__ void enter_group(A &p, uint32_t parts) {
+  const uint32_t g = blockIdx.y;
+  p.x += g * p.g.x;
+  p.data += g * p.g.data;
+  p.scales += g * p.g.scales;
+  p.ts_out += g;
+  p.partial += static_cast<int64_t>(g) * parts;
+}
+
 // ---- pass 1: plain tensor amax ----------------------------------------------------------------------
 struct AmaxArgs {
   const uint8_t *x;
@@ -223,6 +249,7 @@ struct AmaxArgs {
   FastDiv cpr;            // chunks per row
   uint32_t flat;          // rows are contiguous (ldx == row length)
   uint32_t *partial;
+  int64_t g_x;            // bytes between the inputs of consecutive groups (grid dimension y)
 };
 
 template <int ESZ>
@@ -239,6 +266,8 @@ __device__ __forceinline__ void absmax_chunk(const uint4 &v, u16x2 &m2, uint32_t
 template <int ESZ>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs p) {
   constexpr int U = 8;  // loads in flight per lane
+  p.x += blockIdx.y * p.g_x;
+  p.partial += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   const uint32_t stride = gridDim.x * kAmaxThreads;
   u16x2 m2 = {0, 0};
   uint32_t m4 = 0;
@@ -277,10 +306,14 @@ struct RowArgs {
   uint32_t key0, key1, stream_id, sign_word;
   float *rht_out;
   float ts_div;
+  GroupStrides g;
 };
 
 template <int ESZ, int MODE, bool RHT, bool PASS1>
 __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
+  enter_group(p, p.nparts);
+  p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
+  p.stream_id += blockIdx.y;
   const uint32_t stride = gridDim.x * kThreads;
   uint32_t b = blockIdx.x * kThreads + threadIdx.x;
   auto src = [&](uint32_t blk) {
@@ -335,12 +368,10 @@ __device__ __forceinline__ uint32_t codes8(const float (&yv)[8], float e) {
 // fp32 squared error of 8 values against their codes w under scale S, accumulated into acc with fma
 // in order.
 __device__ __forceinline__ float sse8(const float (&yv)[8], uint32_t w, float S, float ts, float acc) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float diff = yv[c] - decode((w >> (4 * c)) & 15u, S, ts);
-    acc = fmaf(diff, diff, acc);
-  }
-  return acc;
+  acc = sse_pair<0>(w, yv[0], yv[1], S, ts, acc);
+  acc = sse_pair<1>(w, yv[2], yv[3], S, ts, acc);
+  acc = sse_pair<2>(w, yv[4], yv[5], S, ts, acc);
+  return sse_pair<3>(w, yv[6], yv[7], S, ts, acc);
 }
 
 // ---- ROW mode, 16x16 tiles --------------------------------------------------------------------------
@@ -356,6 +387,7 @@ struct Row2dArgs {
   uint8_t *scales;
   float *ts_out;
   float ts_div;
+  GroupStrides g;
 };
 
 template <int ESZ>
@@ -394,6 +426,7 @@ __device__ __forceinline__ float tile_sse_rows(const Raw8<ESZ> (&v)[16], float e
 
 template <int ESZ, bool FOS>
 __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
+  enter_group(p, p.nparts);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   const int64_t KB = p.K / 16;
@@ -473,6 +506,7 @@ struct ColArgs {
   uint32_t key0, key1, stream_id, sign_word;
   float *rht_out;
   float ts_div;
+  GroupStrides g;
 };
 
 constexpr int kColTokens = 256;  // per workgroup tile
@@ -480,6 +514,9 @@ constexpr int kColCols = 128;
 
 template <int ESZ, int MODE, bool RHT, bool B2D, bool PASS1, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
+  enter_group(p, p.nparts);
+  p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
+  p.stream_id += blockIdx.y;
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kColCols * (kColTokens / 2)];
   __shared__ __attribute__((aligned(16))) uint8_t lds_scales[kColCols * (kColTokens / 16)];
   const uint32_t ti = threadIdx.x >> 4;  // token group (16 tokens)
@@ -639,7 +676,9 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   if constexpr (PASS1) write_partial(mx, p.partial_out);
 }
 
-__global__ void zero_ts_kernel(float *ts) { *ts = 0.0f; }
+__global__ void zero_ts_kernel(float *ts, uint32_t n) {
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) ts[i] = 0.0f;
+}
 
 // ---- host-side dispatch -------------------------------------------------------------------------------
 uint32_t clamp_grid(uint64_t want, uint64_t cap) {
@@ -660,6 +699,8 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   const uint32_t key0 = static_cast<uint32_t>(a.seed), key1 = static_cast<uint32_t>(a.seed >> 32);
   const uint8_t *x = static_cast<const uint8_t *>(a.x);
   uint32_t nparts = 1;
+  const uint32_t G = static_cast<uint32_t>(a.groups);
+  const GroupStrides gs{a.x_group_bytes, a.R * a.K / 2, b2d ? (a.R / 16) * (a.K / 16) : a.R * (a.K / 16)};
 
   // geometry of the pass-2 kernels (needed for the transform variants of pass 1 as well)
   RowArgs ra{};
@@ -668,13 +709,13 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   if (!colwise) {
     ra = RowArgs{x, ldx_bytes, static_cast<uint32_t>(a.R * (a.K / 16)), make_fastdiv(static_cast<uint32_t>(a.K / 16)), a.K,
                  a.workspace, 0, a.workspace, a.data, a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out,
-                 ts_div};
+                 ts_div, gs};
   } else {
     const uint32_t ntr = static_cast<uint32_t>((a.R + kColCols - 1) / kColCols);
     const uint32_t ntk = static_cast<uint32_t>((a.K + kColTokens - 1) / kColTokens);
     col_tiles = ntr * ntk;
     ca = ColArgs{x, ldx_bytes, a.K, a.R, col_tiles, make_fastdiv(ntr), a.workspace, 0, a.workspace, a.data,
-                 a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out, ts_div};
+                 a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out, ts_div, gs};
   }
 
   // ---- pass 1
@@ -684,14 +725,14 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint64_t total = static_cast<uint64_t>(a.rows) * cpr;
     nparts = clamp_grid((total + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads), kAmaxParts);
     AmaxArgs am{x, ldx_bytes, static_cast<uint32_t>(total), make_fastdiv(cpr > 0 ? cpr : 1),
-                static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace};
-    hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts), dim3(kAmaxThreads), 0, a.stream, am);
+                static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace, a.x_group_bytes};
+    hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts, G), dim3(kAmaxThreads), 0, a.stream, am);
   } else if (!colwise) {
     nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kPass1Parts);
-    hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, true>), dim3(nparts), dim3(kThreads), 0, a.stream, ra);
+    hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, true>), dim3(nparts, G), dim3(kThreads), 0, a.stream, ra);
   } else {
     nparts = clamp_grid(col_tiles, kPass1Parts);
-    hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false>), dim3(nparts), dim3(kThreads), 0, a.stream, ca);
+    hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false>), dim3(nparts, G), dim3(kThreads), 0, a.stream, ca);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -700,7 +741,7 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   if (!colwise && !b2d) {
     ra.nparts = nparts;
     const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, kPass2Grid);
-    const dim3 g(grid), blk(kThreads);
+    const dim3 g(grid, G), blk(kThreads);
 #define NVFP4_ROW(MODE_, RHT_) hipLaunchKernelGGL((row1d_kernel<ESZ, MODE_, RHT_, false>), g, blk, 0, a.stream, ra)
     if (a.rht) {
       if (mode == kSR)
@@ -725,16 +766,16 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   } else if (!colwise && b2d) {
     const uint32_t nseg = static_cast<uint32_t>((a.K + 511) / 512);
     Row2dArgs r2{x, ldx_bytes, static_cast<uint32_t>((a.R / 16) * nseg), make_fastdiv(nseg), a.K, a.workspace, nparts,
-                 a.data, a.scales, a.ts, ts_div};
+                 a.data, a.scales, a.ts, ts_div, gs};
     const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid);
     if (fos)
-      hipLaunchKernelGGL((row2d_kernel<ESZ, true>), dim3(grid), dim3(kThreads), 0, a.stream, r2);
+      hipLaunchKernelGGL((row2d_kernel<ESZ, true>), dim3(grid, G), dim3(kThreads), 0, a.stream, r2);
     else
-      hipLaunchKernelGGL((row2d_kernel<ESZ, false>), dim3(grid), dim3(kThreads), 0, a.stream, r2);
+      hipLaunchKernelGGL((row2d_kernel<ESZ, false>), dim3(grid, G), dim3(kThreads), 0, a.stream, r2);
   } else {
     ca.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
-    const dim3 grid(clamp_grid(col_tiles, kPass2Grid)), block(kThreads);
+    const dim3 grid(clamp_grid(col_tiles, kPass2Grid), G), block(kThreads);
 #define NVFP4_COL(MODE_, RHT_, B2D_)                                                                        \
   do {                                                                                                     \
     if (aligned)                                                                                           \
@@ -773,7 +814,7 @@ hipError_t launch_quantize(const QuantArgs &a) {
   if (a.R == 0 || a.K == 0) {
     // empty tensor: ts = 0, nothing else to write (a kernel, not a memset, so that the call can be
     // captured in a graph)
-    hipLaunchKernelGGL(zero_ts_kernel, dim3(1), dim3(1), 0, a.stream, a.ts);
+    hipLaunchKernelGGL(zero_ts_kernel, dim3(1), dim3(64), 0, a.stream, a.ts, static_cast<uint32_t>(a.groups));
     return hipGetLastError();
   }
   return a.dtype == 1 ? dispatch_quantize<2>(a) : dispatch_quantize<4>(a);

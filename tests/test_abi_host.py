@@ -74,6 +74,25 @@ def test_quantize_validation(rht):
     assert _q(flags=1 << 6, rht=rht) == nv.NVFP4_ERR_UNSUPPORTED
 
 
+def test_quantize_grouped_validation():
+    L = nv.lib()
+
+    def qg(G=4, stride=32 * 64, flags=0, x=FAKE, dtype=nv.NVFP4_BF16, out=None, ws=FAKE):
+        d = out if out is not None else _desc(32, 64, flags)
+        return L.nvfp4_quantize_grouped(x, dtype, G, 32, 64, 64, stride, flags, 0, 0, ctypes.byref(d), ws, None)
+    assert qg(G=0) == nv.NVFP4_ERR_SHAPE
+    assert qg(G=65536) == nv.NVFP4_ERR_SHAPE
+    assert qg(stride=-64) == nv.NVFP4_ERR_SHAPE
+    assert qg(stride=1 << 40) == nv.NVFP4_ERR_SHAPE              # group offsets beyond the 36-bit range
+    assert qg(stride=32 * 64 + 4) == nv.NVFP4_ERR_ALIGN          # 8-byte group step for bf16
+    assert qg(x=None) == nv.NVFP4_ERR_NULL
+    assert qg(ws=None) == nv.NVFP4_ERR_NULL
+    assert qg(x=MIS) == nv.NVFP4_ERR_ALIGN
+    assert qg(out=_desc(32, 48)) == nv.NVFP4_ERR_SHAPE            # descriptor is per group: [32 x 64]
+    assert qg(flags=nv.NVFP4_SR | nv.NVFP4_FOUR_OVER_SIX) == nv.NVFP4_ERR_UNSUPPORTED
+    assert qg(dtype=5) == nv.NVFP4_ERR_UNSUPPORTED
+
+
 def test_rht_rejects_2d_and_block2d_rows():
     assert _q(flags=nv.NVFP4_BLOCK2D, rht=True) == nv.NVFP4_ERR_UNSUPPORTED
     assert _q(flags=nv.NVFP4_BLOCK2D, rows=40, ldx=64) == nv.NVFP4_ERR_SHAPE  # R % 16 for 2D
