@@ -134,3 +134,42 @@ def test_gemm_wgrad8b_rht_sampled_tiles(oracle):
     rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
     print(f"relative error of NVFP4 wgrad vs bf16 inputs on one tile: {rel:.3f}")
     assert rel < 0.35
+
+
+def test_gemm_grouped_beyond_one_launch(oracle):
+    # 200 expert groups (more than one launch's group table holds), empty groups included, weights
+    # from one grouped quantize call; every group checked against the oracle, both output types
+    rng = np.random.default_rng(31)
+    sizes = rng.integers(0, 40, 200)
+    sizes[[0, 127, 128, 199]] = [0, 0, 33, 5]
+    G, N, K = len(sizes), 48, 256
+    M = int(sizes.sum())
+    offs = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    a = synth.normal((M, K), 1.0, seed=31, tensor_id=400)
+    w = torch.stack([synth.normal((N, K), 0.02 * (1 + g % 7), seed=31, tensor_id=401 + g) for g in range(G)])
+    qa = nv.nvfp4_quantize(a.cuda())
+    qb = nv.nvfp4_quantize_grouped(w.cuda())
+    ha, hb = _host(qa), _host(qb)
+    ts_b = qb.tensor_scale.cpu().numpy()
+    for out_dtype in (torch.float32, torch.bfloat16):
+        print(f"[gemm] 200 groups out={out_dtype}", flush=True)
+        c = nv.nvfp4_gemm(qa, qb, out_dtype=out_dtype, group_offsets=offs).float().cpu().numpy()
+        for g in range(G):
+            r0, r1 = offs[g], offs[g + 1]
+            if r1 == r0:
+                continue
+            sub_a = {"data": ha["data"][r0:r1], "scales": ha["scales"][r0:r1], "ts": ha["ts"], "flags": 0}
+            sub_b = {"data": hb["data"][g * N:(g + 1) * N], "scales": hb["scales"][g * N:(g + 1) * N],
+                     "ts": ts_b[g], "flags": 0}
+            cref, bnd = oracle.gemm_ref(sub_a, sub_b, r1 - r0, N, K)
+            gemm_check(c[r0:r1], cref, bnd, out_dtype == torch.bfloat16, f"group {g}")
+    # the same groups with the output quantized in the epilogue: the oracle's quantization of the
+    # fp32 C with the given tensor scale
+    c32 = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32, group_offsets=offs)
+    ts = float(c32.abs().max()) / 2688.0
+    out = nv.empty_like_quantized(M, N, 0, "cuda")
+    out.tensor_scale.fill_(ts)
+    nv.nvfp4_gemm_nvfp4_out(qa, qb, out, group_offsets=offs)
+    data, scales = oracle.quantize_given_ts(c32.cpu().numpy(), np.float32(ts))
+    np.testing.assert_array_equal(out.scales.cpu().numpy(), scales)
+    np.testing.assert_array_equal(out.data.cpu().numpy(), data)
