@@ -16,8 +16,9 @@ bounded sample of the same workload.
 
 Other workloads (--workload): fprop8b_q (the GEMM output quantized in the epilogue), dgrad8b,
 wgrad8b (RHT + stochastic rounding), w4a16_8b and w4a16_decode (bf16 activations x NVFP4 weights),
-fprop405b (the Llama-3.1-405B FFN forward, 8192x53248x16384) and moe (64 experts [4096x1536],
-Zipf(1.1) top-2 loads over 16384 tokens, grouped GEMM).  The CPU oracle baseline is timed on the
+fprop405b (the Llama-3.1-405B FFN forward, 8192x53248x16384), moe (64 experts [4096x1536],
+Zipf(1.1) top-2 loads over 16384 tokens, grouped GEMM) and dequant8b (NVFP4 -> bf16 / fp32 decode of
+the fprop weight and activations, HBM GB/s).  The CPU oracle baseline is timed on the
 default workload only.
 """
 import argparse
@@ -41,7 +42,7 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop8b",
                    choices=["fprop8b", "fprop8b_q", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode",
-                            "fprop405b", "moe"])
+                            "fprop405b", "moe", "dequant8b"])
     p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
@@ -163,6 +164,9 @@ def main():
 
     if a.workload == "moe":
         run_moe(a, nv, torch, synth, dev)
+        return
+    if a.workload == "dequant8b":
+        run_dequant(a, nv, torch, synth, dev)
         return
     if a.workload in ("fprop8b", "fprop8b_q"):
         x_cpu, w_cpu = synth.fprop8b(0)
@@ -426,6 +430,85 @@ def main():
                                        "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)})
     if not a.no_cpu and a.workload == "fprop8b":
         result["cpu_baseline"] = cpu_baseline(a, nv)
+    print(json.dumps(result), flush=True)
+
+
+def run_dequant(a, nv, torch, synth, dev):
+    """nvfp4_dequantize of the fprop shapes: W [14336 x 4096] (16x16 tiles) and X [8192 x 4096] (1D)
+    to bf16, and W to fp32.  One step = the three decodes; algorithmic bytes = codes + scale bytes
+    read, the decoded tensor written."""
+    x_cpu, w_cpu = synth.fprop8b(0)
+    qx = nv.nvfp4_quantize(x_cpu.to(dev))
+    qw = nv.nvfp4_quantize(w_cpu.to(dev), flags=nv.NVFP4_BLOCK2D)
+    del x_cpu, w_cpu
+    yw16 = torch.empty((qw.rows, qw.k), dtype=torch.bfloat16, device=dev)
+    yw32 = torch.empty((qw.rows, qw.k), dtype=torch.float32, device=dev)
+    yx16 = torch.empty((qx.rows, qx.k), dtype=torch.bfloat16, device=dev)
+    calls = [("w_2d_bf16", lambda: nv.nvfp4_dequantize(qw, out=yw16), qw, 2),
+             ("x_1d_bf16", lambda: nv.nvfp4_dequantize(qx, out=yx16), qx, 2),
+             ("w_2d_f32", lambda: nv.nvfp4_dequantize(qw, out=yw32), qw, 4)]
+
+    def nbytes(q, es):
+        return q.data.numel() + q.scales.numel() + q.rows * q.k * es
+
+    def step():
+        for _, fn, _, _ in calls:
+            fn()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    comp = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn, q, es in calls:
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        comp[name + "_ms"] = round(ms, 4)
+        comp[name + "_gbps"] = round(nbytes(q, es) / (ms * 1e-3) / 1e9, 1)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(a.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+    total = sum(nbytes(q, es) for _, _, q, es in calls)
+    gbps = total / (ms_step * 1e-3) / 1e9
+    w16 = comp["w_2d_bf16_gbps"]
+    result = {
+        "metric": "NVFP4 dequantize HBM GB/s",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 x e4m3) -> bf16 / f32",
+        "data": "synthetic",
+        "config": {"workload": "decode of Llama-3-8B FFN fprop operands: W[14336x4096] 16x16 tiles -> bf16 and f32, "
+                               "X[8192x4096] 1D -> bf16"},
+        "components": dict(comp, algorithmic_bytes=total,
+                           step_timing="HIP graph replay of the three decodes; components: mean of back-to-back launches"),
+        "roofline": {"kernel": "nvfp4 dequantize (W 2D -> bf16)", "bound": "hbm", "achieved": w16,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(w16 / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -167,6 +167,28 @@ def test_dequantize_matches_oracle(oracle, flags):
                                   torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy())
 
 
+def test_dequantize_strided_output_and_full_weight(oracle):
+    # into a column window of a wider output (ldy > K), both dtypes: the columns outside stay
+    x = _gauss((48, 160), 10)
+    q, _ = _run(x, 0)
+    ref = oracle.dequantize(q.data.cpu().numpy(), q.scales.cpu().numpy(), q.tensor_scale.item(), 48, 160, 0)
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((48, 160 + 24), 7.0, dtype=dt, device="cuda")
+        nv.nvfp4_dequantize(q, out=big[:, 8:168])
+        got = big.cpu()
+        assert torch.all(got[:, :8] == 7.0) and torch.all(got[:, 168:] == 7.0)
+        want = torch.from_numpy(ref).to(dt)
+        assert torch.equal(got[:, 8:168].view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           want.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+    # the decode of the full 2D-quantized fprop weight [14336 x 4096], as the bench times it
+    _, w = synth.fprop8b(0)
+    qw = nv.nvfp4_quantize(w.cuda(), flags=nv.NVFP4_BLOCK2D)
+    y16 = nv.nvfp4_dequantize(qw, torch.bfloat16).cpu()
+    ref = oracle.dequantize(qw.data.cpu().numpy(), qw.scales.cpu().numpy(), qw.tensor_scale.item(),
+                            qw.rows, qw.k, nv.NVFP4_BLOCK2D)
+    assert torch.equal(y16.view(torch.int16), torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16))
+
+
 def test_round_trip_tiny_workload(oracle):
     a, b = synth.tiny(0)
     for t in (a, b):
