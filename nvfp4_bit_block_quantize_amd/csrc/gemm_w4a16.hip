@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(W4Args p) {
 // ---- few activation rows (decode): weight streaming --------------------------------------------------
 // With M <= 64 the product is bound by reading the weight once from HBM.  A workgroup of W waves owns
 // 64 weight rows (four 16-row tiles) and 16 MT activation rows (all of them for M <= 64; for M up
-// to 192 the grid's second dimension walks 64-row chunks, each a pass over the weight, the later
+// to 256 the grid's second dimension walks 64-row chunks, each a pass over the weight, the later
 // ones mostly from the Infinity Cache); its waves split K, wave w
 // taking the 128-element chunks w, w + W, ... (neighbouring waves read neighbouring bytes of each row),
 // and their partial sums meet in LDS at the end.
@@ -475,9 +475,9 @@ void launch_skinny(const W4A16Args &a, const SkArgs &p) {
 
 hipError_t launch_gemm_w4a16(const W4A16Args &a) {
   // few activation rows, whole 128-element chunks, 8-byte aligned scale rows: weight streaming,
-  // one pass over the weight per 64 activation rows (up to 192 rows: beyond, the tiled kernel's
+  // one pass over the weight per 64 activation rows (up to 256 rows: beyond, the tiled kernel's
   // single pass over the weight wins)
-  if (a.M > 0 && a.M <= 192 && a.N > 0 && a.K > 0 && a.K % 128 == 0 &&
+  if (a.M > 0 && a.M <= 256 && a.N > 0 && a.K > 0 && a.K % 128 == 0 &&
       (reinterpret_cast<uintptr_t>(a.b_scales) & 7u) == 0 && (a.M - 1) * a.lda * 2 + 2 * a.K < (int64_t(1) << 31)) {
     SkArgs p{};
     p.a = static_cast<const uint8_t *>(a.a);

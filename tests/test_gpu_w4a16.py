@@ -50,13 +50,14 @@ def test_w4a16_ragged_shapes(oracle, M, N, K, out_dtype):
     print(f"max |err| / bound = {rel:.3e}")
 
 
-# few activation rows (<= 192) and K % 128 == 0 take the weight-streaming kernel: M tiles 1..4, chunk
+# few activation rows (<= 256) and K % 128 == 0 take the weight-streaming kernel: M tiles 1..4, chunk
 # counts that leave waves idle (K = 128) or uneven (K = 1152), ragged N, 1D and 2D scales; above 64
-# rows, 64-row activation chunks (a ragged last chunk whose missing rows wrap), and 193 rows, the
+# rows, 64-row activation chunks (a ragged last chunk whose missing rows wrap), and 257 rows, the
 # first count past the switch to the tiled kernel
 @pytest.mark.parametrize("M,N,K", [(1, 200, 128), (5, 64, 1152), (16, 1000, 512), (17, 130, 2048),
                                    (33, 64, 256), (64, 336, 1024), (65, 96, 256), (100, 200, 512),
-                                   (128, 64, 1152), (192, 130, 2048), (193, 64, 256)])
+                                   (128, 64, 1152), (192, 130, 2048), (193, 64, 256), (256, 80, 512),
+                                   (257, 64, 256)])
 @pytest.mark.parametrize("b_flags", [0, 2])
 def test_w4a16_few_rows(oracle, M, N, K, b_flags):
     if b_flags and N % 16:
