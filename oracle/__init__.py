@@ -76,6 +76,8 @@ def lib():
         L.or_gemm_ref.restype = ctypes.c_int
         L.or_gemm_w4a16_ref.argtypes = [P, i64, P, P, ctypes.c_float, u32, i64, i64, i64, P, i64, P, P, ctypes.c_int]
         L.or_gemm_w4a16_ref.restype = ctypes.c_int
+        L.or_tile_sse_2d.argtypes = [P, i64, ctypes.c_float, ctypes.c_float, P]
+        L.or_tile_sse_2d.restype = ctypes.c_float
         _LIB = L
     return _LIB
 
@@ -186,6 +188,16 @@ def quantize_given_ts(y, ts, nthreads=None):
     if rc != 0:
         raise ValueError("oracle quantize_given_ts rejected the arguments")
     return data, scales
+
+
+def tile_sse_2d(tile, ts, T):
+    """Four-over-Six error of one 16x16 float32 tile for grid target T under tensor scale ts.
+    Returns (sse as np.float32, scale byte)."""
+    tile = np.asarray(tile)
+    assert tile.dtype == np.float32 and tile.shape == (16, 16) and tile.strides[1] == 4
+    sb = np.zeros(1, dtype=np.uint8)
+    v = lib().or_tile_sse_2d(_p(tile), tile.strides[0] // 4, float(np.float32(ts)), float(T), _p(sb))
+    return np.float32(v), int(sb[0])
 
 
 def dequantize(data, scales, ts, R, K, flags=0):

@@ -72,6 +72,19 @@ struct QuantCtx {
   float ts;
 };
 
+/* Sum of the n x n block at (r, c) of a 16x16 array of squared errors, over the quad tree: the
+ * block splits into four n/2 x n/2 blocks, summed as (top-left + bottom-right) + (top-right +
+ * bottom-left), down to single elements.  Transposing the tile maps the two diagonal blocks
+ * onto themselves and swaps the two off-diagonal ones, so (float addition being commutative)
+ * the tile and its transpose give the same sum. */
+float quad_sum(const float *sq, int r, int c, int n) {
+  if (n == 1) return sq[r * 16 + c];
+  const int h = n / 2;
+  float diag = quad_sum(sq, r, c, h) + quad_sum(sq, r + h, c + h, h);
+  float off = quad_sum(sq, r, c + h, h) + quad_sum(sq, r + h, c, h);
+  return diag + off;
+}
+
 /* Encode one element y of Y at (r, k) under scale byte sb.  Returns the 4-bit code. */
 uint8_t encode_element(const QuantCtx &c, float y, uint8_t sb, int64_t r, int64_t k) {
   float S = or_e4m3_value(sb);
@@ -317,24 +330,17 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
           uint8_t sb = block_scale_byte(ab, 6.0f, ts);
           if (fos) {
             /* Four-over-Six on the tile: the same choice as for a 1D block, with the tile SSE
-             * summed by quadrants (see the header) */
+             * the quad-tree sum of the rounded squares (see the header) */
             auto tile_sse = [&](uint8_t sbx) {
-              float q[2][2];
-              for (int qi = 0; qi < 2; ++qi)
-                for (int qj = 0; qj < 2; ++qj) {
-                  float acc = 0.0f;
-                  for (int64_t r = r0 + 8 * qi; r < r0 + 8 * qi + 8; ++r)
-                    for (int64_t t = 8 * qj; t < 8 * qj + 8; ++t) {
-                      int64_t k = 16 * kb + t;
-                      float y = Y[static_cast<size_t>(r * K + k)];
-                      float diff = y - decode_element(encode_element(c, y, sbx, r, k), sbx, ts);
-                      acc = std::fmaf(diff, diff, acc);
-                    }
-                  q[qi][qj] = acc;
+              float sq[256];
+              for (int i = 0; i < 16; ++i)
+                for (int t = 0; t < 16; ++t) {
+                  int64_t r = r0 + i, k = 16 * kb + t;
+                  float y = Y[static_cast<size_t>(r * K + k)];
+                  float diff = y - decode_element(encode_element(c, y, sbx, r, k), sbx, ts);
+                  sq[i * 16 + t] = diff * diff;
                 }
-              float top = q[0][0] + q[0][1];
-              float bottom = q[1][0] + q[1][1];
-              return top + bottom;
+              return quad_sum(sq, 0, 0, 16);
             };
             const float acc6 = tile_sse(sb);
             const uint8_t sb4 = block_scale_byte(ab, 4.0f, ts);
@@ -412,6 +418,23 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
     sse2[1] = b;
   }
   return 0;
+}
+
+float or_tile_sse_2d(const float *tile, int64_t ld, float ts, float T, uint8_t *sb_out) {
+  float ab = 0.0f;
+  for (int i = 0; i < 16; ++i)
+    for (int t = 0; t < 16; ++t) ab = std::max(ab, std::fabs(tile[i * ld + t]));
+  const uint8_t sb = block_scale_byte(ab, T, ts);
+  QuantCtx c{16, 16, 0u, 0u, 0u, ts};
+  float sq[256];
+  for (int i = 0; i < 16; ++i)
+    for (int t = 0; t < 16; ++t) {
+      float y = tile[i * ld + t];
+      float diff = y - decode_element(encode_element(c, y, sb, i, t), sb, ts);
+      sq[i * 16 + t] = diff * diff;
+    }
+  if (sb_out) *sb_out = sb;
+  return quad_sum(sq, 0, 0, 16);
 }
 
 int or_quantize_given_ts(const float *y, int64_t rows, int64_t cols, int64_t ldy, float ts, uint8_t *data,

@@ -73,10 +73,13 @@ void or_rht16_array(float *u, int64_t nchunks, uint32_t sign_word); /* or_rht16 
  *   rht_out (nullable, only with use_rht) [R][K] fp32 transformed Y
  *   sse2   (nullable) [0] = sum of chosen block SSE, [1] = sum of plain (target 6) block SSE;
  *          filled for FOUR_OVER_SIX and SCALE_SEARCH only
- * Block SSE: fp32, diff = RN(y - xhat), acc = fma(diff, diff, acc) in block order (1D); for a
- * 16x16 tile the four 8x8 quadrants are summed so in row-major order each and combined as
- * RN(RN(S00 + S01) + RN(S10 + S11)) (S_ij: rows 8i.., columns 8j..).  A candidate replaces the
- * current choice only if its SSE is strictly lower (candidates in the order listed above).
+ * Block SSE: fp32, diff = RN(y - xhat), acc = fma(diff, diff, acc) in block order (1D).  For a
+ * 16x16 tile every element contributes RN(diff * diff) and the 256 squares are summed over a
+ * quad tree: each 2n x 2n block is RN(RN(TL + BR) + RN(TR + BL)) of its four n x n blocks (TL:
+ * top-left, BR: bottom-right, ...), down to single elements.  Transposition maps TL and BR onto
+ * themselves and swaps TR with BL, so a tile and its transpose get the same sum and the same
+ * choice: quantizing W^T equals transposing the quantized W.  A candidate replaces the current
+ * choice only if its SSE is strictly lower (candidates in the order listed above).
  * Returns 0 on success, nonzero on an unsupported shape / mode.                                */
 int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
                 uint64_t seed, uint32_t stream_id, int use_rht, uint64_t sign_seed,
@@ -92,6 +95,12 @@ int or_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld
  * data [rows][cols/2], scales [rows][cols/16].  Returns 0, or 2 if cols % 16 != 0.            */
 int or_quantize_given_ts(const float *y, int64_t rows, int64_t cols, int64_t ldy, float ts, uint8_t *data,
                          uint8_t *scales, int nthreads);
+
+/* Four-over-Six tile error of one 16x16 tile (row-major, leading dimension ld) for grid target T
+ * (6 or 4) under tensor scale ts: the block scale of the tile maximum for T (as or_quantize), the
+ * nearest-even codes under it, and the quad-tree sum of the squared errors described above.
+ * *sb_out (nullable) receives the scale byte.  For tests that build near-tie tiles.            */
+float or_tile_sse_2d(const float *tile, int64_t ld, float ts, float T, uint8_t *sb_out);
 
 /* Dequantize to fp32: y[r*K + k] = RN(RN(e2m1 * S) * ts). */
 int or_dequantize(const uint8_t *data, const uint8_t *scales, float ts, int64_t R, int64_t K,

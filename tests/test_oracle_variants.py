@@ -72,15 +72,74 @@ def test_four_over_six_2d_hand_built_tiles(oracle):
     np.testing.assert_array_equal(_codes(fos["data"])[:, 16:], _codes(plain["data"])[:, 16:])
 
 
-def test_four_over_six_2d_never_worse_and_transpose_consistent(oracle):
+def test_four_over_six_2d_never_worse(oracle):
     x = _t(64, 96, 4)
     q = oracle.quantize(x, flags=oracle.BLOCK2D | oracle.FOUR_OVER_SIX)
     assert q["sse"][0] <= q["sse"][1]
-    # the tile SSE adds the quadrants as (top-left + top-right) + (bottom-left + bottom-right), so
-    # the transposed tensor may order its sums differently; the chosen scales agree wherever the
-    # two candidates are not within rounding of each other, and they do on this input
-    qt = oracle.quantize(x, flags=oracle.BLOCK2D | oracle.FOUR_OVER_SIX | oracle.COLWISE)
-    np.testing.assert_array_equal(qt["scales"], q["scales"].T)
+
+
+def _tile_squares(oracle, tile, ts, T):
+    """Rounded squared errors RN(d*d) of a tile under target T, decoded independently of the
+    oracle's quantizer (grid literal, the oracle's E4M3 decode of the tile's scale byte)."""
+    _, sb = oracle.tile_sse_2d(tile, ts, T)
+    S = np.float32(oracle.e4m3_value(sb))
+    e = np.float32(1.0) / np.float32(S * ts)
+    idx = oracle.e2m1_rne_index((np.abs(tile) * e).astype(np.float32)).reshape(16, 16)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    q = np.where(np.signbit(tile), -grid[idx], grid[idx]).astype(np.float32)
+    d = (tile - ((q * S).astype(np.float32) * np.float32(ts)).astype(np.float32)).astype(np.float32)
+    return (d * d).astype(np.float32)
+
+
+def test_tile_error_is_transpose_invariant_sum_of_squares(oracle):
+    """The 2D tile error is a sum of the 256 rounded squares (within fp32 summation error of the
+    exact sum, so no term is dropped or doubled) and does not change, bit for bit, when the tile is
+    transposed, on tiles whose squares span many binades (where the order of additions shows)."""
+    rng = np.random.default_rng(11)
+    ts = np.float32(2.0 ** -10)
+    for trial in range(200):
+        mags = np.exp2(rng.uniform(-12, 0, size=(16, 16)))
+        tile = (rng.choice([-1.0, 1.0], size=(16, 16)) * mags * 2.0).astype(np.float32)
+        for T in (6.0, 4.0):
+            s, _ = oracle.tile_sse_2d(tile, ts, T)
+            st, _ = oracle.tile_sse_2d(np.ascontiguousarray(tile.T), ts, T)
+            assert s.view(np.uint32) == st.view(np.uint32), (trial, T, s, st)
+            sq = _tile_squares(oracle, tile, ts, T).astype(np.float64)
+            exact = float(np.sum(sq))
+            assert abs(float(s) - exact) <= 256 * 2.0 ** -24 * exact, (trial, T, s, exact)
+
+
+def test_four_over_six_2d_transpose_consistent_on_near_ties(oracle):
+    """quantize(W^T) == transpose(quantize(W)) for BLOCK2D | FOUR_OVER_SIX, bit for bit, on random
+    Student-t tiles and on tiles built at the crossing of the two candidates' errors, where a
+    summation order that changes under transposition would decide differently (the witness below
+    counts the tiles a row-major order of the same squares gets wrong)."""
+    from tests.gpu_util import codes
+    from tests.near_tie import TS, near_tie_tensor
+    fl = oracle.BLOCK2D | oracle.FOUR_OVER_SIX
+    for x in (_t(64, 96, 4), near_tie_tensor(oracle, 6, 7, 3)):
+        q = oracle.quantize(x, flags=fl)
+        qt = oracle.quantize(x, flags=fl | oracle.COLWISE)
+        assert qt["ts"] == q["ts"]
+        np.testing.assert_array_equal(qt["scales"], q["scales"].T)
+        np.testing.assert_array_equal(codes(qt["data"]), codes(q["data"]).T)
+    # witness: the near-tie tiles are sharp enough to separate summation orders
+    x = near_tie_tensor(oracle, 6, 7, 3)
+    split = 0
+    for a in range(6):
+        for b in range(7):
+            if a == 0 and b == 0:
+                continue
+            tile = np.ascontiguousarray(x[16 * a:16 * a + 16, 16 * b:16 * b + 16])
+            s6, s4 = _tile_squares(oracle, tile, TS, 6.0), _tile_squares(oracle, tile, TS, 4.0)
+
+            def seq(v):
+                acc = np.float32(0.0)
+                for t in v.ravel():
+                    acc = np.float32(acc + t)
+                return acc
+            split += (seq(s4) < seq(s6)) != (seq(s4.T) < seq(s6.T))
+    assert split >= 5, split
 
 
 def test_variant_combinations_rejected(oracle):
