@@ -365,15 +365,6 @@ __device__ __forceinline__ uint32_t codes8(const float (&yv)[8], float e) {
   return pack8_rne(yv, e);
 }
 
-// fp32 squared error of 8 values against their codes w under scale S, accumulated into acc with fma
-// in order.
-__device__ __forceinline__ float sse8(const float (&yv)[8], uint32_t w, float S, float ts, float acc) {
-  acc = sse_pair<0>(w, yv[0], yv[1], S, ts, acc);
-  acc = sse_pair<1>(w, yv[2], yv[3], S, ts, acc);
-  acc = sse_pair<2>(w, yv[4], yv[5], S, ts, acc);
-  return sse_pair<3>(w, yv[6], yv[7], S, ts, acc);
-}
-
 // ---- ROW mode, 16x16 tiles --------------------------------------------------------------------------
 struct Row2dArgs {
   const uint8_t *x;
@@ -404,24 +395,68 @@ __device__ __forceinline__ void load_patch(Raw8<ESZ> (&v)[16], const uint8_t *__
   }
 }
 
-// Four-over-Six tile error for the lane pair of a 16x16 tile (even lane: columns 0-7, odd lane:
-// columns 8-15, each 16 rows): quadrant sums in row-major order, (TL + TR) + (BL + BR).
-template <int ESZ>
-__device__ __forceinline__ float tile_sse_rows(const Raw8<ESZ> (&v)[16], float e, float S, float ts) {
-  float top = 0.0f, bottom = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    float yv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) yv[c] = raw8_elem<ESZ>(v[t], c);
-    const uint32_t w = codes8(yv, e);
-    if (t < 8)
-      top = sse8(yv, w, S, ts, top);
-    else
-      bottom = sse8(yv, w, S, ts, bottom);
+// ---- Four-over-Six on 16x16 tiles ----------------------------------------------------------------
+// The tile error is the sum of the 256 rounded squares RN(d * d), d = y - RN(RN(q * S) * ts), over a
+// quad tree: a 2n x 2n block is RN(RN(TL + BR) + RN(TR + BL)) of its four n x n blocks, down to
+// single elements.  Transposing a tile keeps TL and BR and swaps TR with BL, so a tile and its
+// transpose (row-wise and column-wise quantization) get the same error and the same choice.
+
+// Rounded squared errors of two elements against their nearest-even codes under factor e / scale S.
+__device__ __forceinline__ f32x2 sq_pair(float y0, float y1, float e, float S, float ts) {
+  uint32_t w;
+  if (__builtin_isinf(e))
+    w = code_degenerate(y0) | (code_degenerate(y1) << 4);
+  else
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0 * e, y1 * e, 1.0f, 0);
+  const f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const float d0 = y0 - (q[0] * S) * ts, d1 = y1 - (q[1] * S) * ts;
+  return f32x2{d0 * d0, d1 * d1};
+}
+
+// Quad-tree sum of the N x N block at (r, c); leaf(r, c) is the sum of the 2 x 2 block at (r, c),
+// (p(r, c) + p(r+1, c+1)) + (p(r, c+1) + p(r+1, c)).
+template <int N, class Leaf>
+__device__ __forceinline__ float quad_sum(const Leaf &leaf, int r, int c) {
+  if constexpr (N == 2) {
+    return leaf(r, c);
+  } else {
+    constexpr int H = N / 2;
+    const float diag = quad_sum<H>(leaf, r, c) + quad_sum<H>(leaf, r + H, c + H);
+    const float off = quad_sum<H>(leaf, r, c + H) + quad_sum<H>(leaf, r + H, c);
+    return diag + off;
   }
+}
+
+// Tile error for the lane pair of a row-wise 16x16 tile: lane holds tile rows 0-15 of columns 0-7
+// (even lane) or 8-15 (odd lane), element (r, c) = column c of v[r].
+template <int ESZ>
+__device__ __forceinline__ float tile_sse_rows(const Raw8<ESZ> (&v)[16], float e, float S, float ts, bool even) {
+  auto leaf = [&](int r, int c) {
+    const f32x2 a = sq_pair(raw8_elem<ESZ>(v[r], c), raw8_elem<ESZ>(v[r], c + 1), e, S, ts);
+    const f32x2 b = sq_pair(raw8_elem<ESZ>(v[r + 1], c), raw8_elem<ESZ>(v[r + 1], c + 1), e, S, ts);
+    return (a[0] + b[1]) + (a[1] + b[0]);
+  };
+  const float top = quad_sum<8>(leaf, 0, 0), bottom = quad_sum<8>(leaf, 8, 0);
   const float top_o = __shfl_xor(top, 1, 64), bottom_o = __shfl_xor(bottom, 1, 64);
-  return (top + top_o) + (bottom + bottom_o);
+  const float tl = even ? top : top_o, tr = even ? top_o : top;
+  const float bl = even ? bottom : bottom_o, br = even ? bottom_o : bottom;
+  return (tl + br) + (tr + bl);
+}
+
+// Tile error for the lane pair of a column-wise 16x16 tile of Y = x^T: lane holds Y rows 0-7 (even
+// lane) or 8-15 (odd lane) of Y columns (tokens) 0-15, element (r, k) = column r of v[k].
+template <int ESZ>
+__device__ __forceinline__ float tile_sse_cols(const Raw8<ESZ> (&v)[16], float e, float S, float ts, bool even) {
+  auto leaf = [&](int r, int k) {
+    const f32x2 a = sq_pair(raw8_elem<ESZ>(v[k], r), raw8_elem<ESZ>(v[k + 1], r), e, S, ts);
+    const f32x2 b = sq_pair(raw8_elem<ESZ>(v[k], r + 1), raw8_elem<ESZ>(v[k + 1], r + 1), e, S, ts);
+    return (a[0] + b[1]) + (a[1] + b[0]);
+  };
+  const float left = quad_sum<8>(leaf, 0, 0), right = quad_sum<8>(leaf, 0, 8);
+  const float left_o = __shfl_xor(left, 1, 64), right_o = __shfl_xor(right, 1, 64);
+  const float tl = even ? left : left_o, tr = even ? right : right_o;
+  const float bl = even ? left_o : left, br = even ? right_o : right;
+  return (tl + br) + (tr + bl);
 }
 
 template <int ESZ, bool FOS>
@@ -456,11 +491,12 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
     float e = encode_factor(S, ts);
     if constexpr (FOS) {
       // Four-over-Six on the tile: target 4 only if its tile error is strictly lower
-      const float sse6 = tile_sse_rows<ESZ>(v, e, S, ts);
+      const bool even = (lane & 1u) == 0;
+      const float sse6 = tile_sse_rows<ESZ>(v, e, S, ts, even);
       float S4;
       const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
       const float e4 = encode_factor(S4, ts);
-      const float sse4 = tile_sse_rows<ESZ>(v, e4, S4, ts);
+      const float sse4 = tile_sse_rows<ESZ>(v, e4, S4, ts, even);
       if (sse4 < sse6) {
         sb = sb4;
         e = e4;
@@ -569,29 +605,13 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       sb2d = block_scale(ab, 6.0f, ts, S2d);
       e2d = encode_factor(S2d, ts);
       if constexpr (MODE == kFourOverSix) {
-        // Four-over-Six on the tile: this lane holds 8 rows (top or bottom half of the tile) of all
-        // 16 columns; quadrant sums in row-major order, (TL + TR) + (BL + BR)
-        auto tile_sse = [&](float e, float S) {
-          float left = 0.0f, right = 0.0f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            float a[8], b[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              a[t] = raw8_elem<ESZ>(v[t], c);
-              b[t] = raw8_elem<ESZ>(v[8 + t], c);
-            }
-            left = sse8(a, codes8(a, e), S, ts, left);
-            right = sse8(b, codes8(b, e), S, ts, right);
-          }
-          const float half = left + right;
-          return half + __shfl_xor(half, 1, 64);
-        };
-        const float sse6 = tile_sse(e2d, S2d);
+        // Four-over-Six on the tile: this lane holds 8 rows (top or bottom half) of the tile
+        const bool even = (tj & 1u) == 0;
+        const float sse6 = tile_sse_cols<ESZ>(v, e2d, S2d, ts, even);
         float S4;
         const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
         const float e4 = encode_factor(S4, ts);
-        const float sse4 = tile_sse(e4, S4);
+        const float sse4 = tile_sse_cols<ESZ>(v, e4, S4, ts, even);
         if (sse4 < sse6) {
           sb2d = sb4;
           S2d = S4;

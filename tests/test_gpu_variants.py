@@ -76,3 +76,21 @@ def test_c4_expert_block_error_report(oracle):
     # the search can only improve on Four-over-Six (same tensor scale, superset of targets)
     assert tot["search {6..4}"][0] <= tot["4/6"][0]
     assert tot["search, ts=amax/1792"][0] <= tot["4/6, ts=amax/1792"][0]
+
+
+def test_four_over_six_2d_transpose_on_near_ties(oracle):
+    """Row-wise and column-wise 16x16-tile Four-over-Six on tiles built at the crossing of the two
+    candidates' errors (tests/near_tie.py), bit-exact against the oracle; nvfp4_transpose of the
+    row-wise result equals the column-wise quantization (quantize(W^T) == quantize(W)^T)."""
+    from tests.near_tie import near_tie_tensor
+    x = torch.from_numpy(near_tie_tensor(oracle, 8, 12, seed=5))  # fp32 [128 x 192]: bf16 would round the ties away
+    xd = x.cuda()
+    q = nv.nvfp4_quantize(xd, flags=B2 | F46)
+    qc = nv.nvfp4_quantize(xd, flags=COL | B2 | F46)
+    qt = nv.nvfp4_transpose(q)
+    torch.cuda.synchronize()
+    assert_quant_equal(q, oracle.quantize(x.numpy(), flags=B2 | F46), "row2d 4/6 near ties")
+    assert_quant_equal(qc, oracle.quantize(x.numpy(), flags=COL | B2 | F46), "col2d 4/6 near ties")
+    assert torch.equal(qt.data.cpu(), qc.data.cpu())
+    assert torch.equal(qt.scales.cpu(), qc.scales.cpu())
+    assert torch.equal(qt.tensor_scale.cpu(), qc.tensor_scale.cpu())
