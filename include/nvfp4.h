@@ -69,8 +69,10 @@ enum {
   /* Four-over-Six (hyper.ai (de) story on the Nemotron 3 Ultra NVFP4 checkpoint): per 1D block,
    * map the block maximum to 6 or to 4, whichever gives the lower block squared error (fp32,
    * fused multiply-add in block order; a tie keeps 6).  ts is unchanged.  With NVFP4_BLOCK2D the
-   * choice is made per 16x16 tile, its squared error summed per 8x8 quadrant in row-major order and
-   * combined as (top-left + top-right) + (bottom-left + bottom-right). */
+   * choice is made per 16x16 tile: each element's squared error is rounded to fp32 and the 256
+   * squares are summed over a quad tree, each 2n x 2n block as (top-left + bottom-right) +
+   * (top-right + bottom-left) of its n x n blocks.  That sum does not change under transposition,
+   * so quantizing W^T (NVFP4_COLWISE) equals transposing the quantized W (nvfp4_transpose). */
   NVFP4_FOUR_OVER_SIX = 1u << 3,
   /* Tensor scale amax / (4 * 448) instead of amax / (6 * 448): a block scale for target 4 then
    * never clamps at the E4M3 maximum (a variant of Four-over-Six; combinable with every mode). */

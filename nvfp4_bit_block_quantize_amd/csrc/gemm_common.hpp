@@ -74,7 +74,7 @@ __device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_
   tm = bi * band + (rem - tn * rows_in_band);
 }
 
-// Epilogue of a 256 x 256 tile: C = ts * acc, where acc[j][i] is the 32 x 32 product of the wave's
+// Epilogue of a 256 x 256 tile: C = (acc * ts_a) * ts_b, where acc[j][i] is the 32 x 32 product of the wave's
 // B fragment j and A fragment i, so lane (h, l32) holds row l32 of tile (i, j), columns
 // 8 (r >> 2) + 4 h + (r & 3).  Whole tiles go through LDS (smem, at least 4 x 32 x 512 bytes, no
 // longer read by any wave's pending loads), 32 rows of the wave's quarter at a time, so that each
@@ -84,8 +84,8 @@ __device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_
 // take element stores.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
-                                             int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts,
-                                             bool vec_store, uint32_t wave, uint32_t lane) {
+                                             int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
+                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane) {
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
@@ -105,8 +105,8 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float v0 = acc[j][i][4 * q] * ts, v1 = acc[j][i][4 * q + 1] * ts;
-          const float v2 = acc[j][i][4 * q + 2] * ts, v3 = acc[j][i][4 * q + 3] * ts;
+          const float v0 = (acc[j][i][4 * q] * ts_a) * ts_b, v1 = (acc[j][i][4 * q + 1] * ts_a) * ts_b;
+          const float v2 = (acc[j][i][4 * q + 2] * ts_a) * ts_b, v3 = (acc[j][i][4 * q + 3] * ts_a) * ts_b;
           if constexpr (OUT_BF16) {
             // v_cvt_pk_bf16_f32: nearest-even, as bf16_rne
             const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
@@ -139,7 +139,7 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
         for (int r = 0; r < 16; ++r) {
           const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
           if (col >= N) continue;
-          const float v = acc[j][i][r] * ts;
+          const float v = (acc[j][i][r] * ts_a) * ts_b;
           if constexpr (OUT_BF16)
             reinterpret_cast<uint16_t *>(c + row * ldc * 2)[col] = static_cast<uint16_t>(bf16_rne(v));
           else
@@ -149,15 +149,15 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
   }
 }
 
-// Quantized epilogue: C = ts_ab * acc (the fp32 values store_c_tile would write) is quantized
+// Quantized epilogue: C = (acc * ts_a) * ts_b (the fp32 values store_c_tile would write) is quantized
 // row-wise in 16-column blocks, nearest-even, with the given tensor scale ts_q: codes to
 // q_data [rows][N / 2], scale bytes to q_scales [rows][N / 16] (N % 16 == 0).  Each wave stages
 // 32 rows x 128 columns of fp32 through LDS (16-byte chunk c of row r at c ^ (r & 31)); lane
 // (row 8 t + (l >> 3), block l & 7) encodes one block per t, so eight lanes write a row's 64 bytes
 // of codes.  Returns the lane's maximum |C| over the blocks it stored.
 __device__ __forceinline__ float store_q_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *q_data, uint8_t *q_scales,
-                                              int64_t N, int64_t m0, int64_t n0, int64_t row_end, float ts_ab,
-                                              float ts_q, uint32_t wave, uint32_t lane) {
+                                              int64_t N, int64_t m0, int64_t n0, int64_t row_end, float ts_a,
+                                              float ts_b, float ts_q, uint32_t wave, uint32_t lane) {
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   // all waves are done with the stages and the last (re-fetch) loads have landed
@@ -176,8 +176,8 @@ __device__ __forceinline__ float store_q_tile(floatx16 (&acc)[4][4], uint8_t *sm
       for (int q = 0; q < 4; ++q) {
         const uint32_t ch = 8 * j + 2 * q + h;
         *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & 31)) * 16) =
-            make_float4(acc[j][i][4 * q] * ts_ab, acc[j][i][4 * q + 1] * ts_ab, acc[j][i][4 * q + 2] * ts_ab,
-                        acc[j][i][4 * q + 3] * ts_ab);
+            make_float4((acc[j][i][4 * q] * ts_a) * ts_b, (acc[j][i][4 * q + 1] * ts_a) * ts_b,
+                        (acc[j][i][4 * q + 2] * ts_a) * ts_b, (acc[j][i][4 * q + 3] * ts_a) * ts_b);
       }
     // the wave reads back its own rows (LDS accesses of one wave complete in order)
 #pragma unroll

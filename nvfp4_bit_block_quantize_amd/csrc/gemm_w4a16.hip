@@ -1,6 +1,6 @@
 // gemm_w4a16.hip -- bf16 activations x NVFP4 weights on the gfx950 matrix cores (the weight-only
 // 4-bit path that serving stacks fall back to on hardware without a native FP4 x FP4 product; NVIDIA
-// Hopper in the pages' account of the Nemotron / DeepSeek NVFP4 checkpoints).
+// Hopper in the pages' account of the Nemotron 3 Ultra NVFP4 checkpoint).
 //
 // C[i][j] = ts_b * sum_k a_ik (q_jk S_jk).  Each weight element is decoded exactly to bf16 with its
 // block scale folded in: q (E2M1, <= 2 significant bits) times S (E4M3, <= 4 bits) has at most 6
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(W4Args p) {
     }
   }
 
-  store_c_tile<OUT_BF16>(acc, smem, p.c, p.ldc, m0, n0, p.M, p.N, *p.b_ts, p.vec_store != 0, wave, lane);
+  store_c_tile<OUT_BF16>(acc, smem, p.c, p.ldc, m0, n0, p.M, p.N, *p.b_ts, 1.0f, p.vec_store != 0, wave, lane);
 }
 
 // ---- few activation rows (decode): weight streaming --------------------------------------------------

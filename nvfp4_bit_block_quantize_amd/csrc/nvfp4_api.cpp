@@ -1,7 +1,11 @@
 // nvfp4_api.cpp -- C ABI front end of libnvfp4.so: argument validation on the host, then the
 // kernel launchers.  Validation never touches the GPU, so every error path can be exercised on a
 // machine without one.
+// The library is built with -fvisibility=hidden: only the declarations of the public header (which
+// fix the visibility of the definitions below) are exported.
+#pragma GCC visibility push(default)
 #include "../../include/nvfp4.h"
+#pragma GCC visibility pop
 
 #include <hip/hip_runtime.h>
 
@@ -94,6 +98,50 @@ int run_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t
   return status_of(nvfp4::launch_quantize(a));
 }
 
+// Shared validation of the NVFP4 x NVFP4 GEMM entry points (shapes, groups, operand pointers).
+int validate_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups, const int64_t *group_row_offsets) {
+  if (!a || !b) return NVFP4_ERR_NULL;
+  if (num_groups < 0 || (num_groups > 1 && !group_row_offsets)) return NVFP4_ERR_SHAPE;
+  const int64_t M = a->rows, N = b->rows, K = a->k;
+  if (M < 0 || N < 0 || K < 0 || b->k != K || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((a->flags & NVFP4_BLOCK2D) && M % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((b->flags & NVFP4_BLOCK2D) && N % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M * K >= kMaxIndex || N * K >= kMaxIndex) return NVFP4_ERR_SHAPE;
+  if (num_groups > 1 || group_row_offsets) {
+    const int32_t G = num_groups < 1 ? 1 : num_groups;
+    if (group_row_offsets[0] != 0 || group_row_offsets[G] != M) return NVFP4_ERR_SHAPE;
+    for (int32_t g = 0; g < G; ++g)
+      if (group_row_offsets[g + 1] < group_row_offsets[g]) return NVFP4_ERR_SHAPE;
+  }
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
+  if (K > 0) {  // (with K == 0 no code or scale is read)
+    if (!a->data || !a->scales || !b->data || !b->scales) return NVFP4_ERR_NULL;
+    if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
+  }
+  return NVFP4_OK;
+}
+
+nvfp4::GemmArgs gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups,
+                          const int64_t *group_row_offsets, void *hip_stream) {
+  nvfp4::GemmArgs g{};
+  g.a_data = a->data;
+  g.a_scales = a->scales;
+  g.a_ts = a->tensor_scale;
+  g.a_2d = (a->flags & NVFP4_BLOCK2D) != 0;
+  g.b_data = b->data;
+  g.b_scales = b->scales;
+  g.b_ts = b->tensor_scale;
+  g.b_2d = (b->flags & NVFP4_BLOCK2D) != 0;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->k;
+  g.num_groups = num_groups < 1 ? 1 : num_groups;
+  g.group_offsets = group_row_offsets;
+  g.stream = static_cast<hipStream_t>(hip_stream);
+  return g;
+}
+
 }  // namespace
 
 namespace nvfp4 {
@@ -167,54 +215,6 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int y_dtype, int64_t ldy, 
   return status_of(nvfp4::launch_dequantize(a));
 }
 
-namespace {
-
-// Shared validation of the NVFP4 x NVFP4 GEMM entry points (shapes, groups, operand pointers).
-int validate_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups, const int64_t *group_row_offsets) {
-  if (!a || !b) return NVFP4_ERR_NULL;
-  if (num_groups < 0 || (num_groups > 1 && !group_row_offsets)) return NVFP4_ERR_SHAPE;
-  const int64_t M = a->rows, N = b->rows, K = a->k;
-  if (M < 0 || N < 0 || K < 0 || b->k != K || K % 16 != 0) return NVFP4_ERR_SHAPE;
-  if ((a->flags & NVFP4_BLOCK2D) && M % 16 != 0) return NVFP4_ERR_SHAPE;
-  if ((b->flags & NVFP4_BLOCK2D) && N % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (M * K >= kMaxIndex || N * K >= kMaxIndex) return NVFP4_ERR_SHAPE;
-  if (num_groups > 1 || group_row_offsets) {
-    const int32_t G = num_groups < 1 ? 1 : num_groups;
-    if (group_row_offsets[0] != 0 || group_row_offsets[G] != M) return NVFP4_ERR_SHAPE;
-    for (int32_t g = 0; g < G; ++g)
-      if (group_row_offsets[g + 1] < group_row_offsets[g]) return NVFP4_ERR_SHAPE;
-  }
-  if (M == 0 || N == 0) return NVFP4_OK;
-  if (!a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
-  if (K > 0) {  // (with K == 0 no code or scale is read)
-    if (!a->data || !a->scales || !b->data || !b->scales) return NVFP4_ERR_NULL;
-    if (!aligned16(a->data) || !aligned16(b->data)) return NVFP4_ERR_ALIGN;
-  }
-  return NVFP4_OK;
-}
-
-nvfp4::GemmArgs gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t num_groups,
-                          const int64_t *group_row_offsets, void *hip_stream) {
-  nvfp4::GemmArgs g{};
-  g.a_data = a->data;
-  g.a_scales = a->scales;
-  g.a_ts = a->tensor_scale;
-  g.a_2d = (a->flags & NVFP4_BLOCK2D) != 0;
-  g.b_data = b->data;
-  g.b_scales = b->scales;
-  g.b_ts = b->tensor_scale;
-  g.b_2d = (b->flags & NVFP4_BLOCK2D) != 0;
-  g.M = a->rows;
-  g.N = b->rows;
-  g.K = a->k;
-  g.num_groups = num_groups < 1 ? 1 : num_groups;
-  g.group_offsets = group_row_offsets;
-  g.stream = static_cast<hipStream_t>(hip_stream);
-  return g;
-}
-
-}  // namespace
-
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, int32_t num_groups,
                const int64_t *group_row_offsets, void *hip_stream) {
   if (!a || !b) return NVFP4_ERR_NULL;
@@ -239,7 +239,8 @@ int nvfp4_gemm_nvfp4_out(const nvfp4_tensor *a, const nvfp4_tensor *b, nvfp4_ten
   int st = validate_gemm(a, b, num_groups, group_row_offsets);
   if (st != NVFP4_OK) return st;
   const int64_t M = a->rows, N = b->rows, K = a->k;
-  if (out->rows != M || out->k != N) return NVFP4_ERR_SHAPE;
+  // C is quantized in 16-column blocks along N: the output's K axis is N
+  if (out->rows != M || out->k != N || N % 16 != 0) return NVFP4_ERR_SHAPE;
   if (out->flags != 0) return NVFP4_ERR_UNSUPPORTED;  // row-wise 1D blocks, nearest-even only
   if (M == 0 || N == 0) return NVFP4_OK;
   // the quantized epilogue lives in the pipelined kernel: whole pairs of 128-element K steps,

@@ -124,7 +124,7 @@ def test_gemm_wgrad8b_rht_sampled_tiles(oracle):
     c = nv.nvfp4_gemm(qa, qb, out_dtype=torch.float32)
     torch.cuda.synchronize()
     M, N, K = qa.rows, qb.rows, qa.k
-    tiles = seeded_tiles(M, N, 32, seed=1)
+    tiles = seeded_tiles(M, N, 64, seed=1) + [(0, 0, 1, N), (M - 1, 0, 1, N)]
     cref, bnd = oracle.gemm_ref(_host(qa), _host(qb), M, N, K, tiles=tiles)
     gemm_check(c.cpu().numpy(), cref, bnd, False, "wgrad 14336x4096x8192")
     # the transforms cancel in the product: dW stays close to the unquantized dY^T X
@@ -134,6 +134,32 @@ def test_gemm_wgrad8b_rht_sampled_tiles(oracle):
     rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
     print(f"relative error of NVFP4 wgrad vs bf16 inputs on one tile: {rel:.3f}")
     assert rel < 0.35
+
+
+@pytest.mark.parametrize("K", [80, 256])
+@pytest.mark.parametrize("case", ["tiny_scales", "huge_spikes"])
+def test_gemm_degenerate_tensor_scales(oracle, case, K):
+    """Tensor scales whose product under- or overflows fp32 while C itself is representable: the
+    epilogue multiplies by ts_a and then by ts_b, never by RN(ts_a * ts_b).  tiny_scales: inputs
+    ~N(0, 2^-116), so ts_a * ts_b falls below the smallest normal fp32 (the product would carry ~15
+    bits); huge_spikes: one 2^76 entry per operand at different k (ts ~ 2^64.6 each, so ts_a * ts_b
+    overflows to inf), every other block's scale underflows to zero and C is exactly 0 (inf * 0
+    would be NaN)."""
+    if case == "tiny_scales":
+        a = synth.normal((96, K), 2.0 ** -58, seed=5, tensor_id=90, dtype=torch.float32)
+        b = synth.normal((80, K), 2.0 ** -58, seed=5, tensor_id=91, dtype=torch.float32)
+    else:
+        a = synth.normal((96, K), 1.0, seed=5, tensor_id=92, dtype=torch.float32)
+        b = synth.normal((80, K), 1.0, seed=5, tensor_id=93, dtype=torch.float32)
+        a[0, 0] = 2.0 ** 76
+        b[0, 1] = 2.0 ** 76
+    ts_a = np.float32(a.abs().max().item()) / np.float32(2688.0)
+    ts_b = np.float32(b.abs().max().item()) / np.float32(2688.0)
+    with np.errstate(over="ignore", under="ignore"):
+        prod = np.float32(ts_a * ts_b)
+    assert (prod < np.float32(2.0 ** -126)) if case == "tiny_scales" else np.isinf(prod)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        _gemm_case(oracle, a, b, out_dtype=out_dtype, what=f"degenerate {case} K={K}")
 
 
 def test_gemm_grouped_beyond_one_launch(oracle):
