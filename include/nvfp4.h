@@ -118,6 +118,19 @@ int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
                    uint32_t flags, uint64_t seed, uint32_t stream_id, nvfp4_tensor *out,
                    void *workspace, void *hip_stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and result, with the
+ * amax pass's workspace in a library-owned 16 KiB device array (one per GPU, held until the process
+ * ends) instead of a caller buffer.  The call allocates nothing; on its first use on a device it
+ * looks the array's address up (hipGetSymbolAddress) with that device current.  Every call on one
+ * GPU shares the array, so calls that may overlap on one GPU (different streams) race: serialise
+ * them or use nvfp4_quantize with distinct workspaces.  Arguments, layouts and errors as
+ * nvfp4_quantize; a shape whose workspace would exceed the array gives NVFP4_ERR_SHAPE (none of the
+ * shapes nvfp4_quantize accepts does). */
+int nvfp4_quantize_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           uint32_t flags, uint64_t seed, uint32_t stream_id, nvfp4_tensor *out,
+                           void *hip_stream);
+
 /* As nvfp4_quantize, after a 16x16 random Hadamard transform of every 16-element block along K
  * (Wgrad inputs: aissential.tech article, Method; hyper.ai (fr) story, "transformation de Hadamard
  * aleatoire").  Each block u becomes (1/4) H16 D u with H16 the Sylvester Hadamard matrix and D the

@@ -23,7 +23,7 @@ __all__ = [
     "NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_UNSUPPORTED",
     "NVFP4_ERR_HIP", "NVFP4_F32", "NVFP4_BF16", "NVFP4_COLWISE", "NVFP4_BLOCK2D", "NVFP4_SR",
     "NVFP4_FOUR_OVER_SIX", "NVFP4_TS_FOR_FOUR", "NVFP4_SCALE_SEARCH", "NVFP4Error", "NVFP4Tensor", "library_path", "lib",
-    "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize",
+    "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_rht_quantize", "nvfp4_dequantize",
     "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_scale_from_amax", "nvfp4_gemm_w4a16", "nvfp4_transpose", "nvfp4_status_string", "empty_like_quantized",
 ]
 
@@ -60,6 +60,8 @@ def lib():
         L.nvfp4_workspace_size.restype = ctypes.c_size_t
         L.nvfp4_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, u32, u64, u32, TP, P, P]
         L.nvfp4_quantize.restype = ctypes.c_int
+        L.nvfp4_quantize_noalloc.argtypes = [P, ctypes.c_int, i64, i64, i64, u32, u64, u32, TP, P]
+        L.nvfp4_quantize_noalloc.restype = ctypes.c_int
         L.nvfp4_rht_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, u32, u64, u32, u64, P, TP, P, P]
         L.nvfp4_rht_quantize.restype = ctypes.c_int
         L.nvfp4_quantize_grouped.argtypes = [P, ctypes.c_int, i64, i64, i64, i64, i64, u32, u64, u32, TP, P, P]
@@ -177,6 +179,17 @@ def nvfp4_quantize(x: torch.Tensor, flags: int = 0, seed: int = 0, stream_id: in
     st = lib().nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), x.shape[0], x.shape[1], _ld(x), flags, seed & (2**64 - 1),
                               stream_id, ctypes.byref(desc), _ptr(workspace), _stream_handle(x.device))
     _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, out: NVFP4Tensor, flags: int = 0, seed: int = 0,
+                           stream_id: int = 0) -> NVFP4Tensor:
+    """nvfp4_quantize into caller-allocated `out`, with the amax workspace in the library's own
+    device array: the call allocates nothing (see include/nvfp4.h)."""
+    desc = out.descriptor()
+    st = lib().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x.dtype), x.shape[0], x.shape[1], _ld(x), flags,
+                                      seed & (2**64 - 1), stream_id, ctypes.byref(desc), _stream_handle(x.device))
+    _check(st, "nvfp4_quantize_noalloc")
     return out
 
 

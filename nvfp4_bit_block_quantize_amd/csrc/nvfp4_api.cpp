@@ -9,6 +9,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "nvfp4_internal.h"
 
 namespace {
@@ -142,6 +144,36 @@ nvfp4::GemmArgs gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, int32_t 
   return g;
 }
 
+// ---- library-owned workspace for nvfp4_quantize_noalloc -----------------------------------------
+// The amax pass's per-workgroup partial maxima live in this file-scope device array (one copy per
+// GPU, held until the process ends) instead of a caller buffer.  Every call rewrites the slots it
+// reads before reading them, so nothing needs clearing; calls that overlap on one GPU share it and
+// race.  Host code never passes the array's name to a kernel (on the host it names a stand-in, not
+// device memory): the device address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+__device__ __align__(256) uint32_t scratch[nvfp4::kMaxParts];
+constexpr size_t kScratchBytes = sizeof(uint32_t) * nvfp4::kMaxParts;
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call per device).
+hipError_t scratch_address(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return *ptr != nullptr ? hipSuccess : hipErrorInvalidSymbol;
+}
+
 }  // namespace
 
 namespace nvfp4 {
@@ -179,6 +211,21 @@ int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
                    uint64_t seed, uint32_t stream_id, nvfp4_tensor *out, void *workspace, void *hip_stream) {
   return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, false, 0, nullptr, out, workspace,
                       hip_stream);
+}
+
+int nvfp4_quantize_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
+                           uint64_t seed, uint32_t stream_id, nvfp4_tensor *out, void *hip_stream) {
+  // the partial maxima never exceed the array (the pass-1 grid is capped at kMaxParts); checked so
+  // that a larger need could not go unnoticed
+  if (nvfp4_workspace_size(rows, cols, flags) > kScratchBytes) return NVFP4_ERR_SHAPE;
+  int64_t R = 0, K = 0;
+  static const uint32_t kAligned[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  // validate with a stand-in workspace pointer first: nothing touches the GPU on an invalid call
+  int st = validate_quantize(x, x_dtype, rows, cols, ldx, flags, false, out, kAligned, &R, &K);
+  if (st != NVFP4_OK) return st;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return NVFP4_ERR_HIP;
+  return run_quantize(x, x_dtype, rows, cols, ldx, flags, seed, stream_id, false, 0, nullptr, out, ws, hip_stream);
 }
 
 int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t flags,
