@@ -111,24 +111,6 @@ __device__ __forceinline__ void encode_block_rne(const float (&y)[16], float ab,
   }
 }
 
-// Stochastic rounding of v >= 0 with 16 random bits r16: between the grid neighbours lo <= v < hi
-// round up iff r16 < f * 65536, f = (v - lo) / (hi - lo) (exact); v >= 6 gives 6.  Both sub-ranges
-// are evaluated and selected (no divergent branches): below 1 the step is 0.5; from 1 up, lo is v with
-// its mantissa cut to one bit and the step is 2^(e-1) for v in [2^e, 2^(e+1)).
-__device__ __forceinline__ uint32_t e2m1_sr_index(float v, uint32_t r16) {
-  const float vc = fminf(v, 6.0f);
-  const uint32_t b = __float_as_uint(vc);
-  const bool small = vc < 1.0f, half = vc >= 0.5f;
-  const float lo = small ? (half ? 0.5f : 0.0f) : __uint_as_float(b & 0xFFC00000u);
-  // 65536 / step: 2^17 below 1, else 2^(17 - e) (the exponent field 271 - biased e; only used when
-  // vc >= 1, where it lies in [129, 144])
-  const float scale = small ? 131072.0f : __uint_as_float((271u - (b >> 23)) << 23);
-  const uint32_t idx = small ? (half ? 1u : 0u) : (b >> 22) - 252u;  // 1 -> 2, 1.5 -> 3, ..., 4 -> 6
-  const float f16 = (vc - lo) * scale;                                // f * 65536, exact
-  const uint32_t r = idx + ((static_cast<float>(r16) < f16) ? 1u : 0u);
-  return v >= 6.0f ? 7u : r;
-}
-
 // ---- Philox4x32-10 -------------------------------------------------------------------------------
 // Counter-based generator of Salmon et al. (SC 2011): ten rounds of two 32x32->64 multiplies with
 // the multipliers 0xD2511F53 / 0xCD9E8D57, key bumped by the Weyl increments 0x9E3779B9 /
@@ -144,8 +126,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     // full 64-bit products: one v_mad_u64_u32 each gives both halves
     const uint64_t p0 = static_cast<uint64_t>(c0) * 0xD2511F53u;
     const uint64_t p1 = static_cast<uint64_t>(c2) * 0xCD9E8D57u;
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    // three-way XORs as one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3, k1, 0x96);
     c0 = n0;
     c1 = static_cast<uint32_t>(p1);
     c2 = n2;
@@ -154,12 +137,6 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     k1 += 0xBB67AE85u;
   }
   return {c0, c1, c2, c3};
-}
-
-// The 16 random bits of element i (logical index r*K + k) live in the Philox block for i >> 3.
-__device__ __forceinline__ uint32_t r16_of(const u32x4 &w, uint32_t j /* i & 7 */) {
-  uint32_t word = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
-  return (word >> (16u * (j & 1u))) & 0xFFFFu;
 }
 
 // ---- 16-point random Hadamard transform (in registers) -------------------------------------------
