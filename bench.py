@@ -663,23 +663,33 @@ def run_moe(a, nv, torch, synth, dev):
 
 
 def cpu_baseline(a, nv):
-    """The CPU oracle (as it stands) on a bounded sample of the step: quantize the first rows of X
-    and of W, then the binary64 GEMM of the two samples over the full K.  Reported in the step's
-    unit (TFLOP/s of 2*m*n*K)."""
+    """The CPU oracle (as it stands) on bounded samples of the workloads, on the host's cores.
+
+    Main sample (the `value`, in the step's unit: TFLOP/s of 2*m*n*K per second of quantize + GEMM):
+    quantize the first rows of X (1D) and of W (16x16 tiles), then the binary64 GEMM of the two
+    samples over the full K, handed to the oracle as 128 x 128 output tiles (its GEMM runs one tile
+    per thread).  Also: the same on one core (an eighth of the rows), the full tiny 64 x 64 x 64
+    round trip, and 64 output tiles of 128 x 128 with the 405B FFN's K = 16384 (operands drawn
+    like that workload's, 1024 rows each)."""
     import numpy as np
     import oracle
     import synth
     threads = max(1, min(16, os.cpu_count() or 1))
+
+    def tiles_of(m, n, t=128):
+        return [(i, j, min(t, m - i), min(t, n - j)) for i in range(0, m, t) for j in range(0, n, t)]
+
     rows = a.cpu_rows
     x_cpu, w_cpu = synth.fprop8b(0)
     xs = synth.bf16_bits(x_cpu[:rows].contiguous())
     wsmp = synth.bf16_bits(w_cpu[:rows].contiguous())
+    del x_cpu, w_cpu
     K = xs.shape[1]
     t0 = time.perf_counter()
     qx = oracle.quantize(xs, nthreads=threads)
     qw = oracle.quantize(wsmp, flags=oracle.BLOCK2D, nthreads=threads)
     t1 = time.perf_counter()
-    oracle.gemm_ref(qx, qw, rows, rows, K, nthreads=threads)
+    oracle.gemm_ref(qx, qw, rows, rows, K, tiles=tiles_of(rows, rows), nthreads=threads)
     t2 = time.perf_counter()
     flops = 2.0 * rows * rows * K
     qbytes = quant_bytes(rows, K, False) + quant_bytes(rows, K, True)
@@ -689,8 +699,26 @@ def cpu_baseline(a, nv):
     qx1 = oracle.quantize(xs[:r1], nthreads=1)
     qw1 = oracle.quantize(wsmp[:r1], flags=oracle.BLOCK2D, nthreads=1)
     s1 = time.perf_counter()
-    oracle.gemm_ref(qx1, qw1, r1, r1, K, nthreads=1)
+    oracle.gemm_ref(qx1, qw1, r1, r1, K, tiles=tiles_of(r1, r1), nthreads=1)
     s2 = time.perf_counter()
+    # the tiny round trip, in full: quantize A and B (fp32 64 x 64), dequantize, GEMM
+    ta, tb = synth.tiny(0)
+    u0 = time.perf_counter()
+    qa, qb = oracle.quantize(ta.numpy(), nthreads=threads), oracle.quantize(tb.numpy(), nthreads=threads)
+    oracle.dequantize(qa["data"], qa["scales"], qa["ts"], 64, 64)
+    oracle.dequantize(qb["data"], qb["scales"], qb["ts"], 64, 64)
+    oracle.gemm_ref(qa, qb, 64, 64, 64, nthreads=threads)
+    u1 = time.perf_counter()
+    # 64 tiles of 128 x 128 with K = 16384 (the 405B FFN's contraction), operands of that workload's
+    # distributions: X ~N(0,1) with 0.1% outlier channels x20, W ~N(0,0.01) in 16x16 tiles
+    xa = synth.normal((1024, 16384), 1.0, seed=0, tensor_id=8)
+    synth.outlier_columns(xa, 0.001, 20.0, seed=0, tensor_id=8)
+    wb = synth.normal((1024, 16384), 0.01, seed=0, tensor_id=9)
+    q5a = oracle.quantize(synth.bf16_bits(xa), nthreads=threads)
+    q5b = oracle.quantize(synth.bf16_bits(wb), flags=oracle.BLOCK2D, nthreads=threads)
+    v0 = time.perf_counter()
+    oracle.gemm_ref(q5a, q5b, 1024, 1024, 16384, tiles=tiles_of(1024, 1024), nthreads=threads)
+    v1 = time.perf_counter()
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -705,13 +733,17 @@ def cpu_baseline(a, nv):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"quantize X[:{rows}] (1D) and W[:{rows}] (2D), binary64 GEMM {rows}x{rows}x{K}",
+        "sample": f"quantize X[:{rows}] (1D) and W[:{rows}] (2D), binary64 GEMM {rows}x{rows}x{K} as 128x128 tiles",
         "seconds": round(t2 - t0, 3),
         "quantize_gbps": round(qbytes / (t1 - t0) / 1e9, 3),
         "gemm_gflops": round(flops / (t2 - t1) / 1e9, 3),
         "one_core": {"sample": f"quantize X[:{r1}], W[:{r1}], GEMM {r1}x{r1}x{K}",
                      "quantize_gbps": round((quant_bytes(r1, K, False) + quant_bytes(r1, K, True)) / (s1 - s0) / 1e9, 3),
                      "gemm_gflops": round(2.0 * r1 * r1 * K / (s2 - s1) / 1e9, 3)},
+        "tiny_round_trip_ms": round((u1 - u0) * 1e3, 3),
+        "k16384_tiles": {"sample": "64 tiles of 128x128, K = 16384 (binary64)",
+                         "seconds": round(v1 - v0, 3),
+                         "gemm_gflops": round(64 * 2.0 * 128 * 128 * 16384 / (v1 - v0) / 1e9, 3)},
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model,
     }

@@ -354,6 +354,22 @@ struct PipeLayout {
 // bank line, so a ds_read_b128 of a fragment is conflict-free.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3u; }
 
+// Scheduling pattern of one sub-step: 16 times one MFMA followed by up to V VALU instructions.
+template <int V>
+__device__ __forceinline__ void mfma_valu_pattern() {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
+// Two E4M3 bytes spread as (b, b, c, c) -> the fp16 pair (S_b, S_b) (HI = false) or (S_c, S_c).
+template <bool HI>
+__device__ __forceinline__ uint32_t scale_pair_cvt(uint32_t spread) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spread, 1.0f, HI));
+}
+
 // Four E4M3 bytes -> four fp16 pairs (S, S).
 __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
   const uint32_t lo = __builtin_amdgcn_perm(w, w, 0x01010000u);  // b0 b0 b1 b1
@@ -387,7 +403,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
   const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
-  const int64_t KT = p.K / 128, KP = KT / 2;  // K steps, pairs of steps
+  const int32_t KT = static_cast<int32_t>(p.K / 128), KP = KT / 2;  // K steps, pairs of steps
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -427,27 +443,28 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   }
   const uint32_t lds_codes = 4096 * wave;                             // + 1024 i
   const uint32_t lds_sc = (is_a ? kPSA : kPSB) + 1024 * (wave & 1);  // + 256 i (not PAIRED)
-  auto issue_codes = [&](uint8_t *st, int64_t kt) {
-    const int64_t kc = kt < KT ? kt : KT - 1;
-    const uint8_t *ga = p.a_data + kc * 64, *gb = b_data + kc * 64;
+  auto issue_codes = [&](uint8_t *st, int32_t kt) {
+    const uint32_t kc = static_cast<uint32_t>(kt < KT ? kt : KT - 1);
+    const uint8_t *ga = p.a_data + kc * 64u, *gb = b_data + kc * 64u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lds_load16(ga + srcA[i], st + kPA + lds_codes + 1024 * i);
       lds_load16(gb + srcB[i], st + kPB + lds_codes + 1024 * i);
     }
     if constexpr (!PAIRED) {
-      const uint8_t *gs = sc_base + kc * 8;
+      const uint8_t *gs = sc_base + kc * 8u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
     }
   };
   // PAIRED, half 0: A's scales of pair pp, half 1: B's; pairs past K re-fetch the last pair
-  auto issue_scales = [&](uint8_t *slot, int64_t pp, int half) {
-    const int64_t pc = pp < KP ? pp : KP - 1;
-    if (half == 0) lds_load16(p.a_scales + pc * 16 + srcSA, slot + 1024 * wave);
-    else lds_load16(b_scales + pc * 16 + srcSB, slot + 4096 + 1024 * wave);
+  auto issue_scales = [&](uint8_t *slot, int32_t pp, int half) {
+    const uint32_t pc = static_cast<uint32_t>(pp < KP ? pp : KP - 1);
+    if (half == 0) lds_load16(p.a_scales + pc * 16u + srcSA, slot + 1024 * wave);
+    else lds_load16(b_scales + pc * 16u + srcSB, slot + 4096 + 1024 * wave);
   };
-  auto slot_of = [&](int64_t pp) { return slots + kPSlot * static_cast<uint32_t>(pp % 3); };
+  // (32-bit: a wave-uniform remainder by 3 is a few scalar instructions, against ~25 in 64 bits)
+  auto slot_of = [&](int32_t pp) { return slots + kPSlot * (static_cast<uint32_t>(pp) % 3u); };
 
   // ---- fragment reads: lane half h takes codes [64 h, 64 h + 64) of the step, chunk q of its half
   const uint32_t rdA = (wm + l32) * 64, rdB = (wn + l32) * 64;
@@ -462,7 +479,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
     }
   };
   // the scale words of step kt (blocks 4 h .. 4 h + 3): out of its pair's slot, or its stage
-  auto read_scales = [&](const uint8_t *src, int64_t kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+  auto read_scales = [&](const uint8_t *src, int32_t kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
     const uint32_t par = PAIRED ? 8 * static_cast<uint32_t>(kt & 1) : 0u;
     constexpr uint32_t kFrag = PAIRED ? 512 : 256;  // 32 rows
 #pragma unroll
@@ -515,12 +532,21 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 
   // one K step out of stage cur: the 8 sub-steps of 16 codes, 16 MFMAs each.  sc_nxt holds the next
   // step's scale pair, sc_tgt receives half of a later pair (distinct slots).
+  // The next step's scale words (read after the barrier in sub-step 4) become fp16 pairs in three
+  // parts, each written over components of psa / psb that this step no longer reads: the decodes of
+  // sub-steps 6 and 7 (issued in iterations 5 and 6) read component 3 only, so components 0 and 1
+  // are converted in iteration 5, component 2 in iteration 6 and component 3 in iteration 7, where
+  // the next step's sub-step 0 is decoded.
   auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt,
-                  const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int64_t kt) {
+                  const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int32_t kt) {
     issue_codes(tgt, kt + 2);
-    if constexpr (PAIRED) issue_scales(sc_tgt, (kt + 4) >> 1, static_cast<int>(kt & 1));
+    if constexpr (PAIRED) issue_scales(sc_tgt, (kt + 4) >> 1, kt & 1);
     read_chunk(cur, pos1, ca1, cb1);
+    // the reads go out now, three sub-steps before their first use (left to itself the compiler
+    // sinks each read next to its use and waits for it there)
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t nsa[4], nsb[4];  // next step's raw scale bytes
+    uint32_t hia[4], hib[4];  // their bytes 2 and 3 spread into pairs
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       half8 afn[4], bfn[4];
@@ -533,13 +559,32 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
           afn[f] = decode8(da, pick(psa[f], mn >> 1));
           bfn[f] = decode8(db, pick(psb[f], mn >> 1));
         }
-      } else {
-        // this step's scales and chunk 0 are dead: ca0 / cb0 hold the next step's chunk 0 (read
-        // after the barrier below) and its scale pairs replace psa / psb
+      }
+      if (m == 5) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          psa[f] = scale_pairs4(nsa[f]);
-          psb[f] = scale_pairs4(nsb[f]);
+          const uint32_t loa = __builtin_amdgcn_perm(nsa[f], nsa[f], 0x01010000u);  // b0 b0 b1 b1
+          const uint32_t lob = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x01010000u);
+          psa[f].x = scale_pair_cvt<false>(loa);
+          psa[f].y = scale_pair_cvt<true>(loa);
+          psb[f].x = scale_pair_cvt<false>(lob);
+          psb[f].y = scale_pair_cvt<true>(lob);
+        }
+      } else if (m == 6) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          hia[f] = __builtin_amdgcn_perm(nsa[f], nsa[f], 0x03030202u);  // b2 b2 b3 b3
+          hib[f] = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x03030202u);
+          psa[f].z = scale_pair_cvt<false>(hia[f]);
+          psb[f].z = scale_pair_cvt<false>(hib[f]);
+        }
+      } else if (m == 7) {
+        // this step's chunk 0 is dead: ca0 / cb0 hold the next step's chunk 0 (read after the
+        // barrier of sub-step 4)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          psa[f].w = scale_pair_cvt<true>(hia[f]);
+          psb[f].w = scale_pair_cvt<true>(hib[f]);
           afn[f] = decode8(ca0[f].x, psa[f].x);
           bfn[f] = decode8(cb0[f].x, psb[f].x);
         }
@@ -549,13 +594,15 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfc[j], afc[i], acc[j][i], 0, 0, 0);
-      // one MFMA, then four decode instructions: the matrix pipe is never left behind a long run of
+      // one MFMA, then the VALU work of the sub-step spread evenly (four decode instructions, five or
+      // six where scale conversions join them): the matrix pipe is never left behind a long run of
       // VALU work (a wave issues in order)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
+      if (m == 5)
+        mfma_valu_pattern<6>();
+      else if (m >= 6)
+        mfma_valu_pattern<5>();
+      else
+        mfma_valu_pattern<4>();
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         afc[f] = afn[f];
@@ -564,17 +611,20 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
       if (m == 4) {
         // every wave holds this step's codes in registers (chunk 1 since sub-step 3's decode), and
         // this lane's loads for step kt + 1 have landed: after the barrier the next stage is complete
-        // and this one may be refilled
+        // and this one may be refilled.  (Fenced on both sides: MFMAs and decodes touch no memory, so
+        // the scheduler would otherwise move the barrier and its waits far up the step.)
+        __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<kLoadsPerStage>();
         wait_lgkmcnt0();
         lds_barrier();
         read_chunk(nxt, pos0, ca0, cb0);
         read_scales(PAIRED ? sc_nxt : nxt, kt + 1, nsa, nsb);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
   uint8_t *cur = st0, *nxt = st1, *tgt = smem + 2 * kPStage;
-  for (int64_t kt = 0; kt < KT; ++kt) {
+  for (int32_t kt = 0; kt < KT; ++kt) {
     if constexpr (PAIRED) step(cur, nxt, tgt, slot_of((kt + 1) >> 1), slot_of((kt + 4) >> 1), kt);
     else step(cur, nxt, tgt, nullptr, nullptr, kt);
     uint8_t *const done = cur;
