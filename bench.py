@@ -42,7 +42,7 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop8b",
                    choices=["fprop8b", "fprop8b_q", "wgrad8b", "dgrad8b", "w4a16_8b", "w4a16_decode",
-                            "fprop405b", "moe", "dequant8b"])
+                            "fprop405b", "moe", "dequant8b", "gemm_designs"])
     p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
@@ -167,6 +167,9 @@ def main():
         return
     if a.workload == "dequant8b":
         run_dequant(a, nv, torch, synth, dev)
+        return
+    if a.workload == "gemm_designs":
+        run_gemm_designs(a, torch, dev)
         return
     if a.workload in ("fprop8b", "fprop8b_q"):
         x_cpu, w_cpu = synth.fprop8b(0)
@@ -431,6 +434,63 @@ def main():
     if not a.no_cpu and a.workload == "fprop8b":
         result["cpu_baseline"] = cpu_baseline(a, nv)
     print(json.dumps(result), flush=True)
+
+
+def run_gemm_designs(a, torch, dev):
+    """The GEMM design probe (libnvfp4_probe.so): the inner step of each way of putting the NVFP4
+    block-scaled product on the matrix cores, timed on its own (operands in registers, no memory
+    traffic) on every SIMD of the GPU: one wave computes a 128 x 128 tile over one 16-element block,
+    repeated.  Design 0 (the library's): exact fp16 decode with the scale folded in +
+    v_mfma_f32_32x32x16_f16.  Design 1: fp4 operands of v_mfma_scale_f32_32x32x64_f8f6f4 (the block
+    zero-padded to 64 K) into a fresh accumulator, rescaled by S_a * S_b per output element.
+    Also design 0's MFMAs alone (operands decoded once), which separates the decode's cost from the
+    matrix cores' own rate.  Useful work: 2 * 128 * 128 * 16 flops per wave per repetition."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "nvfp4_bit_block_quantize_amd", "libnvfp4_probe.so"))
+    P = ctypes.c_void_p
+    L.nvfp4_probe_design.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P]
+    g = torch.Generator(device="cpu").manual_seed(1)
+    codes = [torch.randint(0, 256, (128, 8), dtype=torch.uint8, generator=g).to(dev) for _ in range(2)]
+    scales = [torch.randint(0x30, 0x50, (128, 1), dtype=torch.uint8, generator=g).to(dev) for _ in range(2)]
+    c = torch.zeros((128, 128), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (codes[0], scales[0], codes[1], scales[1])]
+    workgroups, reps = 1024, 2000  # 4 waves each: 4096 waves, 16 per CU
+    out = {}
+    # 0-2: 4 x 4 tiles per wave, 4 waves per workgroup; 3, 5: 2 x 4 tiles, 8 waves (two per SIMD);
+    # 4: 2 x 4 tiles, 4 waves
+    waves = {0: 4, 1: 4, 2: 4, 3: 8, 4: 4, 5: 8}
+    tile_flops = {0: 2 * 128 * 128 * 16, 1: 2 * 128 * 128 * 16, 2: 2 * 128 * 128 * 16,
+                  3: 2 * 64 * 128 * 16, 4: 2 * 64 * 128 * 16, 5: 2 * 64 * 128 * 16}
+    for design in (0, 1, 2, 3, 4, 5):
+        for _ in range(a.warmup):
+            L.nvfp4_probe_design(design, *ptrs, ctypes.c_void_p(c.data_ptr()), reps, workgroups, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            st = L.nvfp4_probe_design(design, *ptrs, ctypes.c_void_p(c.data_ptr()), reps, workgroups, stream)
+        e1.record()
+        e1.synchronize()
+        if st != 0:
+            raise SystemExit(f"probe launch failed: {st}")
+        ms = e0.elapsed_time(e1) / a.steps
+        flops = float(waves[design]) * workgroups * reps * tile_flops[design]
+        out[design] = (ms, flops / (ms * 1e-3) / 1e12)
+    print(json.dumps({
+        "metric": "GEMM design probe: inner-step TFLOP/s of useful work (one 16-element block per step)",
+        "value": round(out[0][1], 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(out[0][0], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 codes", "data": "synthetic",
+        "config": {"workload": "GEMM design probe: 4096 waves x 2000 repetitions of a 128x128x16 block step"},
+        "components": {"design0_fp16_decode_ms": round(out[0][0], 4), "design0_tflops": round(out[0][1], 1),
+                       "design1_fp4_rescale_ms": round(out[1][0], 4), "design1_tflops": round(out[1][1], 1),
+                       "design0_over_design1": round(out[1][0] / out[0][0], 2),
+                       "mfma_alone_ms": round(out[2][0], 4), "mfma_alone_tflops": round(out[2][1], 1),
+                       "tile64x128_two_waves_per_simd_tflops": round(out[3][1], 1),
+                       "tile64x128_one_wave_per_simd_tflops": round(out[4][1], 1),
+                       "tile64x128_mfma_alone_two_waves_tflops": round(out[5][1], 1)},
+    }), flush=True)
 
 
 def run_dequant(a, nv, torch, synth, dev):

@@ -20,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libnvfp4.so")
+# the GEMM design probe (measurement only, not part of the library): bench.py --workload gemm_designs
+PROBE_OUT = os.path.join(HERE, "libnvfp4_probe.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
@@ -66,16 +68,19 @@ def _compile(unit, verbose, changed_only):
 
 def build(verbose=False, changed_only=False):
     os.makedirs(BUILD, exist_ok=True)
-    us = units()
+    us = units() + [("probe_designs.hip", "probe_designs.hip.o", [])]
     # the largest units first, so that they do not start last
     us.sort(key=lambda u: 0 if u[0] in ("gemm_variant.hip", "quantize.hip", "gemm_w4a16.hip") else 1)
     with cf.ThreadPoolExecutor(max_workers=max(1, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda u: _compile(u, verbose, changed_only), us))
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fvisibility=hidden", *objs, "-o", OUT + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(OUT + ".tmp", OUT)
+    probe = [o for o in objs if o.endswith("probe_designs.hip.o")]
+    lib_objs = [o for o in objs if o not in probe]
+    for out, parts in ((OUT, lib_objs), (PROBE_OUT, probe)):
+        cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fvisibility=hidden", *parts, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
     return OUT
 
 
