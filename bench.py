@@ -459,10 +459,13 @@ def run_gemm_designs(a, torch, dev):
     out = {}
     # 0-2: 4 x 4 tiles per wave, 4 waves per workgroup; 3, 5: 2 x 4 tiles, 8 waves (two per SIMD);
     # 4: 2 x 4 tiles, 4 waves
-    waves = {0: 4, 1: 4, 2: 4, 3: 8, 4: 4, 5: 8}
+    # 6: 4 x 4 tiles, one wave per SIMD, design 2 plus decode work the MFMAs do not read
+    # 7: design 0 with the decode of the next block interleaved with the MFMAs of this one
+    waves = {0: 4, 1: 4, 2: 4, 3: 8, 4: 4, 5: 8, 6: 4, 7: 4}
     tile_flops = {0: 2 * 128 * 128 * 16, 1: 2 * 128 * 128 * 16, 2: 2 * 128 * 128 * 16,
-                  3: 2 * 64 * 128 * 16, 4: 2 * 64 * 128 * 16, 5: 2 * 64 * 128 * 16}
-    for design in (0, 1, 2, 3, 4, 5):
+                  3: 2 * 64 * 128 * 16, 4: 2 * 64 * 128 * 16, 5: 2 * 64 * 128 * 16, 6: 2 * 128 * 128 * 16,
+                  7: 2 * 128 * 128 * 16}
+    for design in (0, 1, 2, 3, 4, 5, 6, 7):
         for _ in range(a.warmup):
             L.nvfp4_probe_design(design, *ptrs, ctypes.c_void_p(c.data_ptr()), reps, workgroups, stream)
         torch.cuda.synchronize()
@@ -489,7 +492,9 @@ def run_gemm_designs(a, torch, dev):
                        "mfma_alone_ms": round(out[2][0], 4), "mfma_alone_tflops": round(out[2][1], 1),
                        "tile64x128_two_waves_per_simd_tflops": round(out[3][1], 1),
                        "tile64x128_one_wave_per_simd_tflops": round(out[4][1], 1),
-                       "tile64x128_mfma_alone_two_waves_tflops": round(out[5][1], 1)},
+                       "tile64x128_mfma_alone_two_waves_tflops": round(out[5][1], 1),
+                       "independent_decode_one_wave_tflops": round(out[6][1], 1),
+                       "pipelined_decode_one_wave_tflops": round(out[7][1], 1)},
     }), flush=True)
 
 

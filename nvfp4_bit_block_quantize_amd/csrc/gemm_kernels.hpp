@@ -354,13 +354,16 @@ struct PipeLayout {
 // bank line, so a ds_read_b128 of a fragment is conflict-free.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3u; }
 
-// Scheduling pattern of one sub-step: 16 times one MFMA followed by up to V VALU instructions.
-template <int V>
+// Scheduling pattern of one sub-step: 16 times one MFMA followed by up to V VALU instructions, and
+// L direct loads, one after each of MFMAs 0, 4, 8 ...: issuing a step's loads back to back stalls the
+// wave (the memory pipeline takes them one at a time) while no MFMA is queued.
+template <int V, int L = 0>
 __device__ __forceinline__ void mfma_valu_pattern() {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if (q % 4 == 0 && q / 4 < L) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
   }
 }
 
@@ -457,6 +460,14 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
       for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
     }
   };
+  // piece i of issue_codes: A's and B's code rows 16 i .. 16 i + 15 of each wave's 64 (and, not
+  // PAIRED, the i-th scale load)
+  auto issue_piece = [&](uint8_t *st, int32_t kt, int i) {
+    const uint32_t kc = static_cast<uint32_t>(kt < KT ? kt : KT - 1);
+    lds_load16(p.a_data + kc * 64u + srcA[i], st + kPA + lds_codes + 1024 * i);
+    lds_load16(b_data + kc * 64u + srcB[i], st + kPB + lds_codes + 1024 * i);
+    if constexpr (!PAIRED) lds_load4(sc_base + kc * 8u + srcS[i], st + lds_sc + 256 * i);
+  };
   // PAIRED, half 0: A's scales of pair pp, half 1: B's; pairs past K re-fetch the last pair
   auto issue_scales = [&](uint8_t *slot, int32_t pp, int half) {
     const uint32_t pc = static_cast<uint32_t>(pp < KP ? pp : KP - 1);
@@ -539,8 +550,6 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   // the next step's sub-step 0 is decoded.
   auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt,
                   const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int32_t kt) {
-    issue_codes(tgt, kt + 2);
-    if constexpr (PAIRED) issue_scales(sc_tgt, (kt + 4) >> 1, kt & 1);
     read_chunk(cur, pos1, ca1, cb1);
     // the reads go out now, three sub-steps before their first use (left to itself the compiler
     // sinks each read next to its use and waits for it there)
@@ -589,6 +598,13 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
           bfn[f] = decode8(cb0[f].x, psb[f].x);
         }
       }
+      // the loads of step kt + 2 (into the stage of step kt - 1, free since the barrier of step
+      // kt - 1), a quarter per sub-step 0-3: all are issued before this step's barrier
+      if (m < 4) {
+        issue_piece(tgt, kt + 2, m);
+        if constexpr (PAIRED)
+          if (m == 0) issue_scales(sc_tgt, (kt + 4) >> 1, kt & 1);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -601,6 +617,10 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
         mfma_valu_pattern<6>();
       else if (m >= 6)
         mfma_valu_pattern<5>();
+      else if (m == 0)
+        mfma_valu_pattern<4, 3>();
+      else if (m < 4)
+        mfma_valu_pattern<4, PAIRED ? 2 : 3>();
       else
         mfma_valu_pattern<4>();
 #pragma unroll

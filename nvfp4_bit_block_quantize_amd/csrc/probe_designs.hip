@@ -74,7 +74,10 @@ __device__ __forceinline__ void write_tile(const floatx16 (&acc)[4][4], float *c
 
 // Design 0 on a wave tile of TM x TN MFMA tiles (the library's is 4 x 4), NT threads per workgroup
 // (256: one wave per SIMD; 512: two, which a 2 x 4 tile's 128 accumulators allow).
-template <int TM, int TN, bool DECODE, int NT>
+// DECODE: 1 = each use decodes its operands (the library's K loop), 0 = the MFMAs alone on operands
+// decoded once, 2 = the MFMAs on operands decoded once plus the same decode work on other registers
+// (independent of the MFMAs: whether a wave's VALU work overlaps its own MFMAs at all).
+template <int TM, int TN, int DECODE, int NT>
 __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
   const uint32_t lane = threadIdx.x & 63u, l32 = lane & 31u, h = lane >> 5;
   // this lane's codes of K 8h .. 8h + 7 (one dword) and its row's scale, per A and B fragment
@@ -105,7 +108,14 @@ __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
 #pragma unroll
   for (int f = 0; f < TN; ++f) bf[f] = decode8(cb[f], sb[f]);
   for (int rep = 0; rep < p.reps; ++rep) {
-    if constexpr (DECODE) {
+    half8 ta[TM], tb[TN];  // DECODE == 2: decoded values that no MFMA reads
+    if constexpr (DECODE == 2) {
+      // codes that change with the repetition (one v_xor), so the decode cannot be hoisted
+#pragma unroll
+      for (int f = 0; f < TM; ++f) ta[f] = decode8(ca[f] ^ static_cast<uint32_t>(rep), sa[f]);
+#pragma unroll
+      for (int f = 0; f < TN; ++f) tb[f] = decode8(cb[f] ^ static_cast<uint32_t>(rep), sb[f]);
+    } else if constexpr (DECODE == 1) {
       // the decode of every use, as in the library's K loop (the codes differ from block to block)
 #pragma unroll
       for (int f = 0; f < TM; ++f) {
@@ -128,8 +138,76 @@ __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    if constexpr (DECODE == 2) {
+      // one MFMA, then its share of the decode instructions, throughout
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 9 * (TM + TN) / (TM * TN), 0);
+      }
+#pragma unroll
+      for (int f = 0; f < TM; ++f) opaque(ta[f]);
+#pragma unroll
+      for (int f = 0; f < TN; ++f) opaque(tb[f]);
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x < 64) write_tile<TM, TN>(acc, p.c, lane);
+}
+
+// Design 0 software-pipelined, as the library's K loop: the decode of repetition r + 1 (codes that
+// change with r, one v_xor) is interleaved with the MFMAs of repetition r, one MFMA then its share
+// of the decode instructions (4 x 4 tile, one wave per SIMD).
+__global__ __launch_bounds__(256, 1) void probe_fp16_pipelined(ProbeArgs p) {
+  const uint32_t lane = threadIdx.x & 63u, l32 = lane & 31u, h = lane >> 5;
+  uint32_t ca[4], cb[4];
+  half2v sa[4], sb[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const uint32_t row = 32 * f + l32;
+    ca[f] = reinterpret_cast<const uint32_t *>(p.a_codes + row * 8)[h];
+    cb[f] = reinterpret_cast<const uint32_t *>(p.b_codes + row * 8)[h];
+    const _Float16 s_a = static_cast<_Float16>(e4m3_value(p.a_scales[row]));
+    const _Float16 s_b = static_cast<_Float16>(e4m3_value(p.b_scales[row]));
+    sa[f] = half2v{s_a, s_a};
+    sb[f] = half2v{s_b, s_b};
+  }
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+  half8 af[4], bf[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    af[f] = decode8(ca[f], sa[f]);
+    bf[f] = decode8(cb[f], sb[f]);
+  }
+  half8 an[4], bn[4];
+  // MFMAs on (ac, bc) interleaved with the decode of the next block into (ad, bd)
+  auto block = [&](const half8 (&ac)[4], const half8 (&bc)[4], half8 (&ad)[4], half8 (&bd)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      uint32_t da = ca[f], db = cb[f];
+      opaque(da);
+      opaque(db);
+      ad[f] = decode8(da, sa[f]);
+      bd[f] = decode8(db, sb[f]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ac[i], bc[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  };
+  for (int rep = 0; rep < p.reps; rep += 2) {  // (reps even)
+    block(af, bf, an, bn);
+    block(an, bn, af, bf);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 64) write_tile(acc, p.c, lane);
 }
 
 __global__ __launch_bounds__(256, 1) void probe_fp4_rescale(ProbeArgs p) {
@@ -181,8 +259,9 @@ __global__ __launch_bounds__(256, 1) void probe_fp4_rescale(ProbeArgs p) {
 // design: 0 = fp16 decode + f16 MFMA, 1 = fp4 MFMA + per-block rescale, 2 = the f16 MFMAs of
 // design 0 alone (operands decoded once: the cost of the decode is the difference); on a 2 x 4 wave
 // tile (64 x 128): 3 = design 0 with two waves per SIMD, 4 = design 0 with one, 5 = design 2 with
-// two.  Designs 0-2 run workgroups of 4 waves (one per SIMD), 3-5 of 8 or 4; every wave runs the same
-// step; returns 0, or the HIP error code of the launch.
+// two; 6 = design 2 plus design 0's decode work on registers the MFMAs do not read (4 x 4 tile, one
+// wave per SIMD); 7 = design 0 software-pipelined (4 x 4 tile, one wave per SIMD).  Designs 0-2 and 6 run workgroups of 4 waves (one per SIMD), 3-5 of 8 or 4; every
+// wave runs the same step; returns 0, or the HIP error code of the launch.
 extern "C" __attribute__((visibility("default"))) int nvfp4_probe_design(int design, const uint8_t *a_codes,
                                                                          const uint8_t *a_scales, const uint8_t *b_codes,
                                                                          const uint8_t *b_scales, float *c, int reps,
@@ -193,15 +272,19 @@ extern "C" __attribute__((visibility("default"))) int nvfp4_probe_design(int des
   // waves per SIMD are exactly 2 (512 threads) or 1 (256)
   const size_t one_per_cu = 96 * 1024;
   if (design == 0)
-    hipLaunchKernelGGL((probe_fp16_decode<4, 4, true, 256>), dim3(workgroups), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((probe_fp16_decode<4, 4, 1, 256>), dim3(workgroups), dim3(256), 0, st, p);
   else if (design == 2)
-    hipLaunchKernelGGL((probe_fp16_decode<4, 4, false, 256>), dim3(workgroups), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((probe_fp16_decode<4, 4, 0, 256>), dim3(workgroups), dim3(256), 0, st, p);
   else if (design == 3)
-    hipLaunchKernelGGL((probe_fp16_decode<2, 4, true, 512>), dim3(workgroups), dim3(512), one_per_cu, st, p);
+    hipLaunchKernelGGL((probe_fp16_decode<2, 4, 1, 512>), dim3(workgroups), dim3(512), one_per_cu, st, p);
   else if (design == 4)
-    hipLaunchKernelGGL((probe_fp16_decode<2, 4, true, 256>), dim3(workgroups), dim3(256), one_per_cu, st, p);
+    hipLaunchKernelGGL((probe_fp16_decode<2, 4, 1, 256>), dim3(workgroups), dim3(256), one_per_cu, st, p);
   else if (design == 5)
-    hipLaunchKernelGGL((probe_fp16_decode<2, 4, false, 512>), dim3(workgroups), dim3(512), one_per_cu, st, p);
+    hipLaunchKernelGGL((probe_fp16_decode<2, 4, 0, 512>), dim3(workgroups), dim3(512), one_per_cu, st, p);
+  else if (design == 6)
+    hipLaunchKernelGGL((probe_fp16_decode<4, 4, 2, 256>), dim3(workgroups), dim3(256), 0, st, p);
+  else if (design == 7)
+    hipLaunchKernelGGL(probe_fp16_pipelined, dim3(workgroups), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(probe_fp4_rescale, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
