@@ -74,7 +74,18 @@ __device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_
   tm = bi * band + (rem - tn * rows_in_band);
 }
 
-// Epilogue of a 256 x 256 tile: C = (acc * ts_a) * ts_b, where acc[j][i] is the 32 x 32 product of the wave's
+// C = acc * ts_a * ts_b per element: one multiply by ts_a * ts_b where that product is a normal fp32
+// number (each element is then within one rounding of the exact product), else (acc * ts_a) * ts_b,
+// so that a product of the two tensor scales that under- or overflows never reaches C.  (s1, s2) =
+// (ts_a * ts_b, 1) or (ts_a, ts_b): the two-multiply form only where the product is not normal.
+__device__ __forceinline__ void epilogue_scales(float ts_a, float ts_b, float &s1, float &s2, bool &one) {
+  const float t = ts_a * ts_b;
+  one = __builtin_isnormal(t);
+  s1 = one ? t : ts_a;
+  s2 = one ? 1.0f : ts_b;
+}
+
+// Epilogue of a 256 x 256 tile: C = acc * ts_a * ts_b, where acc[j][i] is the 32 x 32 product of the wave's
 // B fragment j and A fragment i, so lane (h, l32) holds row l32 of tile (i, j), columns
 // 8 (r >> 2) + 4 h + (r & 3).  Whole tiles go through LDS (smem, at least 4 x 32 x 512 bytes, no
 // longer read by any wave's pending loads), 32 rows of the wave's quarter at a time, so that each
@@ -82,10 +93,12 @@ __device__ __forceinline__ void band_tile(int32_t local, int32_t tiles_n, int32_
 // row segments per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row);
 // rows at or beyond row_end are not written.  Tiles cut by N, or C without 16-byte aligned rows,
 // take element stores.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
+template <bool OUT_BF16, bool ONE>
+__device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
                                              float ts_b, bool vec_store, uint32_t wave, uint32_t lane) {
+  // ONE: ts_a is the product of the two tensor scales (see epilogue_scales)
+  auto sc = [&](float v) { return ONE ? v * ts_a : (v * ts_a) * ts_b; };
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
@@ -105,8 +118,8 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float v0 = (acc[j][i][4 * q] * ts_a) * ts_b, v1 = (acc[j][i][4 * q + 1] * ts_a) * ts_b;
-          const float v2 = (acc[j][i][4 * q + 2] * ts_a) * ts_b, v3 = (acc[j][i][4 * q + 3] * ts_a) * ts_b;
+          const float v0 = sc(acc[j][i][4 * q]), v1 = sc(acc[j][i][4 * q + 1]);
+          const float v2 = sc(acc[j][i][4 * q + 2]), v3 = sc(acc[j][i][4 * q + 3]);
           if constexpr (OUT_BF16) {
             // v_cvt_pk_bf16_f32: nearest-even, as bf16_rne
             const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
@@ -139,7 +152,7 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
         for (int r = 0; r < 16; ++r) {
           const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
           if (col >= N) continue;
-          const float v = (acc[j][i][r] * ts_a) * ts_b;
+          const float v = sc(acc[j][i][r]);
           if constexpr (OUT_BF16)
             reinterpret_cast<uint16_t *>(c + row * ldc * 2)[col] = static_cast<uint16_t>(bf16_rne(v));
           else
@@ -149,7 +162,20 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
   }
 }
 
-// Quantized epilogue: C = (acc * ts_a) * ts_b (the fp32 values store_c_tile would write) is quantized
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
+                                             int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
+                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane) {
+  float s1, s2;
+  bool one;
+  epilogue_scales(ts_a, ts_b, s1, s2, one);
+  if (one)
+    store_c_rows<OUT_BF16, true>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane);
+  else
+    store_c_rows<OUT_BF16, false>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane);
+}
+
+// Quantized epilogue: C = acc * ts_a * ts_b (the fp32 values store_c_tile would write) is quantized
 // row-wise in 16-column blocks, nearest-even, with the given tensor scale ts_q: codes to
 // q_data [rows][N / 2], scale bytes to q_scales [rows][N / 16] (N % 16 == 0).  Each wave stages
 // 32 rows x 128 columns of fp32 through LDS (16-byte chunk c of row r at c ^ (r & 31)); lane
@@ -168,6 +194,9 @@ __device__ __forceinline__ float store_q_tile(floatx16 (&acc)[4][4], uint8_t *sm
   uint8_t *const region = smem + wave * (32 * ROWB);
   const int64_t qrow = N / 2, srow = N / 16;
   float amax = 0.0f;
+  float s1, s2;  // (v * s1) * s2 is the value store_c_tile writes (v * ts_a * ts_b when s2 == 1)
+  bool one;
+  epilogue_scales(ts_a, ts_b, s1, s2, one);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -176,8 +205,8 @@ __device__ __forceinline__ float store_q_tile(floatx16 (&acc)[4][4], uint8_t *sm
       for (int q = 0; q < 4; ++q) {
         const uint32_t ch = 8 * j + 2 * q + h;
         *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & 31)) * 16) =
-            make_float4((acc[j][i][4 * q] * ts_a) * ts_b, (acc[j][i][4 * q + 1] * ts_a) * ts_b,
-                        (acc[j][i][4 * q + 2] * ts_a) * ts_b, (acc[j][i][4 * q + 3] * ts_a) * ts_b);
+            make_float4((acc[j][i][4 * q] * s1) * s2, (acc[j][i][4 * q + 1] * s1) * s2,
+                        (acc[j][i][4 * q + 2] * s1) * s2, (acc[j][i][4 * q + 3] * s1) * s2);
       }
     // the wave reads back its own rows (LDS accesses of one wave complete in order)
 #pragma unroll

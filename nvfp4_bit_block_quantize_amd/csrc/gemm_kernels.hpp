@@ -653,8 +653,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
     tgt = done;
   }
 
-  // ---- epilogue: C = (acc * ts_a) * ts_b (never forming ts_a * ts_b, which may under- or overflow
-  // where C does not)
+  // ---- epilogue: C = acc * ts_a * ts_b (one multiply where ts_a * ts_b is a normal number)
   const float ts_a = *p.a_ts, ts_b = p.b_ts[p.group_base + g];
   if constexpr (OUT == 2) {
     float amax = store_q_tile(acc, smem, p.q_data, p.q_scales, p.N, m0, n0, row_end, ts_a, ts_b, *p.q_ts, wave, lane);
