@@ -461,11 +461,12 @@ def run_gemm_designs(a, torch, dev):
     # 4: 2 x 4 tiles, 4 waves
     # 6: 4 x 4 tiles, one wave per SIMD, design 2 plus decode work the MFMAs do not read
     # 7: design 0 with the decode of the next block interleaved with the MFMAs of this one
-    waves = {0: 4, 1: 4, 2: 4, 3: 8, 4: 4, 5: 8, 6: 4, 7: 4}
+    # 8: design 6 with conversions only (independent VALU instructions)
+    waves = {0: 4, 1: 4, 2: 4, 3: 8, 4: 4, 5: 8, 6: 4, 7: 4, 8: 4}
     tile_flops = {0: 2 * 128 * 128 * 16, 1: 2 * 128 * 128 * 16, 2: 2 * 128 * 128 * 16,
                   3: 2 * 64 * 128 * 16, 4: 2 * 64 * 128 * 16, 5: 2 * 64 * 128 * 16, 6: 2 * 128 * 128 * 16,
-                  7: 2 * 128 * 128 * 16}
-    for design in (0, 1, 2, 3, 4, 5, 6, 7):
+                  7: 2 * 128 * 128 * 16, 8: 2 * 128 * 128 * 16}
+    for design in (0, 1, 2, 3, 4, 5, 6, 7, 8):
         for _ in range(a.warmup):
             L.nvfp4_probe_design(design, *ptrs, ctypes.c_void_p(c.data_ptr()), reps, workgroups, stream)
         torch.cuda.synchronize()
@@ -494,7 +495,8 @@ def run_gemm_designs(a, torch, dev):
                        "tile64x128_one_wave_per_simd_tflops": round(out[4][1], 1),
                        "tile64x128_mfma_alone_two_waves_tflops": round(out[5][1], 1),
                        "independent_decode_one_wave_tflops": round(out[6][1], 1),
-                       "pipelined_decode_one_wave_tflops": round(out[7][1], 1)},
+                       "pipelined_decode_one_wave_tflops": round(out[7][1], 1),
+                       "independent_conversions_one_wave_tflops": round(out[8][1], 1)},
     }), flush=True)
 
 

@@ -16,13 +16,26 @@ namespace {
 
 using namespace gemm;
 
-hipError_t launch_gemm_variant(int out, bool a2d, bool b2d, const GemmKArgs &p, int32_t tiles, bool full, bool paired,
+hipError_t launch_gemm_variant(int out, bool a2d, bool b2d, const GemmKArgs &p, int32_t grid, bool full, bool paired,
                                hipStream_t stream) {
 #define NVFP4_CASE(OUT, A2D, B2D) \
-  if (out == OUT && a2d == A2D && b2d == B2D) return launch_variant<OUT, A2D, B2D>(p, tiles, full, paired, stream);
+  if (out == OUT && a2d == A2D && b2d == B2D) return launch_variant<OUT, A2D, B2D>(p, grid, full, paired, stream);
   NVFP4_GEMM_VARIANTS(NVFP4_CASE)
 #undef NVFP4_CASE
   return hipErrorInvalidValue;
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int32_t compute_units() {
+  static int32_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -78,7 +91,16 @@ hipError_t launch_gemm(const GemmArgs &a) {
     // (the entry point admits the quantized output only where the paired pipelined kernel applies)
     if (quant && !paired) return hipErrorInvalidValue;
     const int out = quant ? 2 : (bf16 ? 1 : 0);
-    hipError_t err = launch_gemm_variant(out, a.a_2d, a.b_2d, p, tiles, full, paired, a.stream);
+    // The pipelined kernel with bf16 C and at least four K steps runs each workgroup over several
+    // tiles (one workgroup per compute unit, a multiple of 8 so that every workgroup keeps its XCD):
+    // the next tile's first steps load under the last steps of the current one, and no workgroup
+    // launch separates them.  Otherwise one workgroup per tile.
+    int32_t grid = tiles;
+    if (full && out == 1 && a.K / 128 >= 4) {
+      const int32_t cus = compute_units() / 8 * 8;
+      if (cus >= 8 && cus < tiles) grid = cus;
+    }
+    hipError_t err = launch_gemm_variant(out, a.a_2d, a.b_2d, p, grid, full, paired, a.stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -96,17 +96,23 @@ __device__ __forceinline__ void epilogue_scales(float ts_a, float ts_b, float &s
 template <bool OUT_BF16, bool ONE>
 __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
-                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane) {
+                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
+                                             bool settle) {
   // ONE: ts_a is the product of the two tensor scales (see epilogue_scales)
   auto sc = [&](float v) { return ONE ? v * ts_a : (v * ts_a) * ts_b; };
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
+  // (lane through an opaque copy: in a kernel that runs several tiles, the epilogue's per-lane
+  // addresses are then formed here and not hoisted out of the tile loop into spilled registers)
+  asm volatile("" : "+v"(lane));
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   if (vec_store && n0 + BN <= N) {
-    // all waves are done with the stages and the last (re-fetch) loads have landed
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    lds_barrier();
+    if (settle) {
+      // all waves are done with the stages and the last (re-fetch) loads have landed
+      wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      lds_barrier();
+    }
     constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
     uint8_t *const region = smem + wave * (32 * ROWB);
     uint8_t *const gbase = c + ((m0 + wm) * ldc + n0 + wn) * ES;
@@ -162,17 +168,20 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
   }
 }
 
+// settle = false: smem is a region (waves x 32 x 128 B per element byte) that no wave reads and no
+// load in flight writes, so the staging neither waits for loads nor needs a barrier first.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
-                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane) {
+                                             float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
+                                             bool settle = true) {
   float s1, s2;
   bool one;
   epilogue_scales(ts_a, ts_b, s1, s2, one);
   if (one)
-    store_c_rows<OUT_BF16, true>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane);
+    store_c_rows<OUT_BF16, true>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
   else
-    store_c_rows<OUT_BF16, false>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane);
+    store_c_rows<OUT_BF16, false>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
 }
 
 // Quantized epilogue: C = acc * ts_a * ts_b (the fp32 values store_c_tile would write) is quantized

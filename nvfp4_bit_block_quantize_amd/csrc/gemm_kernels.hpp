@@ -394,19 +394,35 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   uint8_t *const st0 = smem, *const st1 = smem + kPStage;
   uint8_t *const slots = smem + L::kScales;
 
-  const int32_t tile = xcd_tile(blockIdx.x, p.total_tiles);
-  int32_t g = 0;
-  while (g + 1 < p.groups && p.tile_begin[g + 1] <= tile) ++g;
-  const int32_t local = tile - p.tile_begin[g];
-  const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
-  int32_t tm, tn;
-  band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
-  const int64_t row_end = p.row_begin[g + 1];
-  const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
-  const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
-  const int64_t m0 = p.row_begin[g] + static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int32_t KT = static_cast<int32_t>(p.K / 128), KP = KT / 2;  // K steps, pairs of steps
+  // The workgroup's tiles: the s-th is tile_at(s) (launches with fewer workgroups than tiles run
+  // each workgroup over several; every workgroup keeps its XCD).
+  const int32_t nwg = static_cast<int32_t>(gridDim.x);
+  auto tile_at = [&](int32_t s) {
+    const int32_t v = static_cast<int32_t>(blockIdx.x) + s * nwg;
+    return v < p.total_tiles ? xcd_tile(v, p.total_tiles) : -1;
+  };
+  struct TileRef {  // (rows of A and of B are below 2^31)
+    int32_t g, m0, n0, row_end;
+    const uint8_t *b_data, *b_scales;
+  };
+  auto describe = [&](int32_t tile) {
+    TileRef t;
+    int32_t g = 0;
+    while (g + 1 < p.groups && p.tile_begin[g + 1] <= tile) ++g;
+    const int32_t local = tile - p.tile_begin[g];
+    const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
+    int32_t tm, tn;
+    band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
+    t.g = g;
+    t.row_end = static_cast<int32_t>(p.row_begin[g + 1]);
+    t.b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
+    t.b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
+    t.m0 = static_cast<int32_t>(p.row_begin[g]) + tm * BM;
+    t.n0 = tn * BN;
+    return t;
+  };
+  TileRef cur_t = describe(tile_at(0));
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -416,66 +432,87 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   // ---- direct-load sources: 32-bit per-lane offsets (an operand is below 2 GiB) from per-step bases
   const int64_t row_bytes = p.K / 2, KB = p.K / 16;
   uint32_t srcA[4], srcB[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t R = 64 * wave + 16 * i + (lane >> 2);  // tile row this lane fetches
-    const uint32_t c = (lane & 3) ^ swz(R);               // logical chunk stored at position lane & 3
-    const int64_t ra = min(m0 + R, row_end - 1), rb = min(n0 + R, p.N - 1);
-    srcA[i] = static_cast<uint32_t>(ra * row_bytes + 16 * c);
-    srcB[i] = static_cast<uint32_t>(rb * row_bytes + 16 * c);
-  }
   // PAIRED scale pairs: wave w fetches rows [64 w, 64 w + 64) of A's (even steps) or B's (odd steps)
   // slot.  Otherwise [256 rows][8 B] per operand per step: waves 0-1 stage A's, waves 2-3 B's, 64
   // dwords per load.
   uint32_t srcSA, srcSB, srcS[4];
-  {
-    const int64_t ra = min(m0 + 64 * wave + lane, row_end - 1), rb = min(n0 + 64 * wave + lane, p.N - 1);
-    srcSA = static_cast<uint32_t>(A2D ? (ra / 16) * KB : ra * KB);
-    srcSB = static_cast<uint32_t>(B2D ? (rb / 16) * KB : rb * KB);
-  }
   const bool is_a = wave < 2;
-  const uint8_t *sc_base = is_a ? p.a_scales : b_scales;
-  {
-    const int64_t r0 = is_a ? m0 : n0, r_end = is_a ? row_end : p.N;
-    const bool two_d = is_a ? A2D : B2D;
+  // The per-lane offsets are kept as 32-bit values under a scalar base: each use goes through an
+  // opaque copy, and the lane-derived terms are formed afresh where a tile's offsets are formed, so
+  // that the compiler holds neither 64-bit addresses nor the lane terms across the K loop.
+  auto opaque_u32 = [](uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  // the code sources (and, not PAIRED, the scale sources) of tile t
+  auto code_sources = [&](const TileRef &t) {
+    const uint32_t ln = opaque_u32(lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t r = min(r0 + 32 * (4 * (wave & 1) + i) + (lane >> 1), r_end - 1);
-      srcS[i] = static_cast<uint32_t>((two_d ? (r / 16) * KB : r * KB) + 4 * (lane & 1));
+      const uint32_t R = 64 * wave + 16 * i + (ln >> 2);  // tile row this lane fetches
+      const uint32_t c = (ln & 3) ^ swz(R);                 // logical chunk stored at position lane & 3
+      const int64_t ra = min(static_cast<int64_t>(t.m0) + R, static_cast<int64_t>(t.row_end) - 1);
+      const int64_t rb = min(static_cast<int64_t>(t.n0) + R, p.N - 1);
+      srcA[i] = static_cast<uint32_t>(ra * row_bytes + 16 * c);
+      srcB[i] = static_cast<uint32_t>(rb * row_bytes + 16 * c);
     }
-  }
+    if constexpr (!PAIRED) {
+      const int64_t r0 = is_a ? t.m0 : t.n0, r_end = is_a ? static_cast<int64_t>(t.row_end) : p.N;
+      const bool two_d = is_a ? A2D : B2D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = min(r0 + 32 * (4 * (wave & 1) + i) + (ln >> 1), r_end - 1);
+        srcS[i] = static_cast<uint32_t>((two_d ? (r / 16) * KB : r * KB) + 4 * (ln & 1));
+      }
+    }
+  };
+  auto pair_sources = [&](const TileRef &t) {
+    const uint32_t ln = opaque_u32(lane);
+    const int64_t ra = min(static_cast<int64_t>(t.m0) + 64 * wave + ln, static_cast<int64_t>(t.row_end) - 1);
+    const int64_t rb = min(static_cast<int64_t>(t.n0) + 64 * wave + ln, p.N - 1);
+    srcSA = static_cast<uint32_t>(A2D ? (ra / 16) * KB : ra * KB);
+    srcSB = static_cast<uint32_t>(B2D ? (rb / 16) * KB : rb * KB);
+  };
+  code_sources(cur_t);
+  if constexpr (PAIRED) pair_sources(cur_t);
   const uint32_t lds_codes = 4096 * wave;                             // + 1024 i
   const uint32_t lds_sc = (is_a ? kPSA : kPSB) + 1024 * (wave & 1);  // + 256 i (not PAIRED)
   auto issue_codes = [&](uint8_t *st, int32_t kt) {
     const uint32_t kc = static_cast<uint32_t>(kt < KT ? kt : KT - 1);
-    const uint8_t *ga = p.a_data + kc * 64u, *gb = b_data + kc * 64u;
+    const uint8_t *ga = p.a_data + kc * 64u, *gb = cur_t.b_data + kc * 64u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lds_load16(ga + srcA[i], st + kPA + lds_codes + 1024 * i);
       lds_load16(gb + srcB[i], st + kPB + lds_codes + 1024 * i);
     }
     if constexpr (!PAIRED) {
-      const uint8_t *gs = sc_base + kc * 8u;
+      const uint8_t *gs = (is_a ? p.a_scales : cur_t.b_scales) + kc * 8u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_load4(gs + srcS[i], st + lds_sc + 256 * i);
     }
   };
-  // piece i of issue_codes: A's and B's code rows 16 i .. 16 i + 15 of each wave's 64 (and, not
-  // PAIRED, the i-th scale load)
-  auto issue_piece = [&](uint8_t *st, int32_t kt, int i) {
-    const uint32_t kc = static_cast<uint32_t>(kt < KT ? kt : KT - 1);
-    lds_load16(p.a_data + kc * 64u + srcA[i], st + kPA + lds_codes + 1024 * i);
-    lds_load16(b_data + kc * 64u + srcB[i], st + kPB + lds_codes + 1024 * i);
-    if constexpr (!PAIRED) lds_load4(sc_base + kc * 8u + srcS[i], st + lds_sc + 256 * i);
+  // piece i of a K step's loads: A's and B's code rows 16 i .. 16 i + 15 of each wave's 64 (and, not
+  // PAIRED, the i-th scale load), step kc of the tile whose B codes / B scales start at gb / gsb
+  auto issue_piece = [&](uint8_t *st, const uint8_t *gb, const uint8_t *gsb, uint32_t kc, int i) {
+    lds_load16(p.a_data + kc * 64u + opaque_u32(srcA[i]), st + kPA + lds_codes + 1024 * i);
+    lds_load16(gb + kc * 64u + opaque_u32(srcB[i]), st + kPB + lds_codes + 1024 * i);
+    if constexpr (!PAIRED)
+      lds_load4((is_a ? p.a_scales : gsb) + kc * 8u + opaque_u32(srcS[i]), st + lds_sc + 256 * i);
   };
-  // PAIRED, half 0: A's scales of pair pp, half 1: B's; pairs past K re-fetch the last pair
+  // PAIRED, half 0: A's scales of pair pc, half 1: B's (of the tile whose B scales start at gsb)
+  auto issue_pair = [&](uint8_t *slot, const uint8_t *gsb, uint32_t pc, int half) {
+    if (half == 0) lds_load16(p.a_scales + pc * 16u + opaque_u32(srcSA), slot + 1024 * wave);
+    else lds_load16(gsb + pc * 16u + opaque_u32(srcSB), slot + 4096 + 1024 * wave);
+  };
+  // the prologue's pairs 0 and 1 (a pair past K re-fetches the last pair)
   auto issue_scales = [&](uint8_t *slot, int32_t pp, int half) {
-    const uint32_t pc = static_cast<uint32_t>(pp < KP ? pp : KP - 1);
-    if (half == 0) lds_load16(p.a_scales + pc * 16u + srcSA, slot + 1024 * wave);
-    else lds_load16(b_scales + pc * 16u + srcSB, slot + 4096 + 1024 * wave);
+    issue_pair(slot, cur_t.b_scales, static_cast<uint32_t>(pp < KP ? pp : KP - 1), half);
   };
+  // Scale pairs are numbered on across the workgroup's tiles (pair P of its s-th tile is pair
+  // s KP + P), so the ring of slots runs on from tile to tile; pair_base = (s KP) mod 3.
   // (32-bit: a wave-uniform remainder by 3 is a few scalar instructions, against ~25 in 64 bits)
-  auto slot_of = [&](int32_t pp) { return slots + kPSlot * (static_cast<uint32_t>(pp) % 3u); };
+  uint32_t pair_base = 0;
+  auto slot_of = [&](int32_t pp) { return slots + kPSlot * ((pair_base + static_cast<uint32_t>(pp)) % 3u); };
 
   // ---- fragment reads: lane half h takes codes [64 h, 64 h + 64) of the step, chunk q of its half
   const uint32_t rdA = (wm + l32) * 64, rdB = (wn + l32) * 64;
@@ -524,22 +561,25 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   lds_barrier();
   uint4 ca0[4], cb0[4], ca1[4], cb1[4];  // chunk 0 / chunk 1 codes of the current step
   uint4 psa[4], psb[4];                   // fp16 scale pairs of the current step (blocks 4h..4h+3)
-  {
+  half8 afc[4], bfc[4];                   // the current sub-step's decoded fragments
+  // a tile's step 0 (in stage st, its scale pair 0 in slot sc, both complete): its first chunk and
+  // scales read and its sub-step 0 decoded
+  auto start_tile = [&](const uint8_t *st, const uint8_t *sc) {
     uint32_t rsa[4], rsb[4];
-    read_chunk(st0, pos0, ca0, cb0);
-    read_scales(PAIRED ? slots : st0, 0, rsa, rsb);
+    read_chunk(st, pos0, ca0, cb0);
+    read_scales(PAIRED ? sc : st, 0, rsa, rsb);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       psa[f] = scale_pairs4(rsa[f]);
       psb[f] = scale_pairs4(rsb[f]);
     }
-  }
-  half8 afc[4], bfc[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    afc[f] = decode8(ca0[f].x, psa[f].x);
-    bfc[f] = decode8(cb0[f].x, psb[f].x);
-  }
+    for (int f = 0; f < 4; ++f) {
+      afc[f] = decode8(ca0[f].x, psa[f].x);
+      bfc[f] = decode8(cb0[f].x, psb[f].x);
+    }
+  };
+  start_tile(st0, slots);
 
   // one K step out of stage cur: the 8 sub-steps of 16 codes, 16 MFMAs each.  sc_nxt holds the next
   // step's scale pair, sc_tgt receives half of a later pair (distinct slots).
@@ -548,8 +588,26 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   // sub-steps 6 and 7 (issued in iterations 5 and 6) read component 3 only, so components 0 and 1
   // are converted in iteration 5, component 2 in iteration 6 and component 3 in iteration 7, where
   // the next step's sub-step 0 is decoded.
+  // Steps and pairs past the tile's K are the next tile's first ones (nxt_t, where it has one: its
+  // sources replace this tile's from the step that first loads for it on, step KT - 4 for the scale
+  // pairs and KT - 2 for the codes), else a re-fetch of the last step / pair into a stage or slot
+  // that is never consumed.
+  TileRef nxt_t = cur_t;
+  bool has_next = false;
+  // (tail: one of the tile's last four steps, the only ones that may load past its K; the others
+  // are a loop of their own that holds no state of the next tile)
   auto step = [&](uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt, uint8_t *__restrict__ tgt,
-                  const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int32_t kt) {
+                  const uint8_t *__restrict__ sc_nxt, uint8_t *__restrict__ sc_tgt, int32_t kt, bool tail) {
+    // what this step loads: codes of step kt + 2 and (PAIRED) half kt & 1 of pair (kt + 4) / 2
+    const int32_t jc = kt + 2, jp = (kt + 4) >> 1;
+    const bool c_next = tail && has_next && jc >= KT, p_next = tail && has_next && jp >= KP;
+    const uint32_t kc = static_cast<uint32_t>(!tail || jc < KT ? jc : (c_next ? jc - KT : KT - 1));
+    const uint32_t pc = static_cast<uint32_t>(!tail || jp < KP ? jp : (p_next ? jp - KP : KP - 1));
+    const uint8_t *const gb = c_next ? nxt_t.b_data : cur_t.b_data;
+    const uint8_t *const gsb = (PAIRED ? p_next : c_next) ? nxt_t.b_scales : cur_t.b_scales;
+    if (tail && has_next && kt == KT - 2) code_sources(nxt_t);
+    if constexpr (PAIRED)
+      if (tail && has_next && kt == KT - 4) pair_sources(nxt_t);
     read_chunk(cur, pos1, ca1, cb1);
     // the reads go out now, three sub-steps before their first use (left to itself the compiler
     // sinks each read next to its use and waits for it there)
@@ -601,9 +659,9 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
       // the loads of step kt + 2 (into the stage of step kt - 1, free since the barrier of step
       // kt - 1), a quarter per sub-step 0-3: all are issued before this step's barrier
       if (m < 4) {
-        issue_piece(tgt, kt + 2, m);
+        issue_piece(tgt, gb, gsb, kc, m);
         if constexpr (PAIRED)
-          if (m == 0) issue_scales(sc_tgt, (kt + 4) >> 1, kt & 1);
+          if (m == 0) issue_pair(sc_tgt, gsb, pc, kt & 1);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -644,43 +702,81 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
     }
   };
   uint8_t *cur = st0, *nxt = st1, *tgt = smem + 2 * kPStage;
-  for (int32_t kt = 0; kt < KT; ++kt) {
-    if constexpr (PAIRED) step(cur, nxt, tgt, slot_of((kt + 1) >> 1), slot_of((kt + 4) >> 1), kt);
-    else step(cur, nxt, tgt, nullptr, nullptr, kt);
-    uint8_t *const done = cur;
-    cur = nxt;
-    nxt = tgt;
-    tgt = done;
-  }
+  const float ts_a = *p.a_ts;
+  for (int32_t s = 0;; ++s) {
+    // (bf16 C only, and with at least four K steps: the tile's C is staged in the one free stage,
+    // and the next tile's first scale pair is fetched from step KT - 4 on)
+    auto run_steps = [&](int32_t k0, int32_t k1, bool tail) __attribute__((always_inline)) {
+      for (int32_t kt = k0; kt < k1; ++kt) {
+        if constexpr (PAIRED) step(cur, nxt, tgt, slot_of((kt + 1) >> 1), slot_of((kt + 4) >> 1), kt, tail);
+        else step(cur, nxt, tgt, nullptr, nullptr, kt, tail);
+        uint8_t *const done = cur;
+        cur = nxt;
+        nxt = tgt;
+        tgt = done;
+      }
+    };
+    const int32_t k_tail = KT > 4 ? KT - 4 : 0;
+    run_steps(0, k_tail, false);
+    const int32_t next_tile = (OUT == 1 && KT >= 4) ? tile_at(s + 1) : -1;
+    has_next = next_tile >= 0;
+    if (has_next) nxt_t = describe(next_tile);
+    run_steps(k_tail, KT, true);
 
-  // ---- epilogue: C = acc * ts_a * ts_b (one multiply where ts_a * ts_b is a normal number)
-  const float ts_a = *p.a_ts, ts_b = p.b_ts[p.group_base + g];
-  if constexpr (OUT == 2) {
-    float amax = store_q_tile(acc, smem, p.q_data, p.q_scales, p.N, m0, n0, row_end, ts_a, ts_b, *p.q_ts, wave, lane);
-    if (p.amax != nullptr) {
-      // non-negative floats order like their bit patterns: one atomic max per wave
+    // ---- epilogue: C = acc * ts_a * ts_b (one multiply where ts_a * ts_b is a normal number)
+    const float ts_b = p.b_ts[p.group_base + cur_t.g];
+    if constexpr (OUT == 2) {
+      float amax = store_q_tile(acc, smem, p.q_data, p.q_scales, p.N, cur_t.m0, cur_t.n0, cur_t.row_end, ts_a, ts_b,
+                                *p.q_ts, wave, lane);
+      if (p.amax != nullptr) {
+        // non-negative floats order like their bit patterns: one atomic max per wave
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-      if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(p.amax), __float_as_uint(amax));
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(p.amax), __float_as_uint(amax));
+      }
+    } else if (!has_next) {
+      store_c_tile<OUT == 1>(acc, smem, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
+                             p.vec_store != 0, wave, lane);
+    } else {
+      // staged in tgt, the stage of the tile's last step: read by no wave since that step's barrier
+      // and the target of the next tile's first loads, so every wave's read-back completes before
+      // the barrier after it; the next tile's loads in flight are not waited for
+      store_c_tile<OUT == 1>(acc, tgt, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
+                             p.vec_store != 0, wave, lane, false);
+      wait_lgkmcnt0();
+      lds_barrier();
     }
-  } else {
-    store_c_tile<OUT == 1>(acc, smem, p.c, p.ldc, m0, n0, row_end, p.N, ts_a, ts_b, p.vec_store != 0, wave, lane);
+    if (!has_next) break;
+    // the next tile: its steps 0 and 1 and scale pairs 0 and 1 are loaded (step 0 and pair 0
+    // complete since the last step's barrier), so its start is read again from LDS (cheaper than
+    // holding the last step's reads of it in registers through the epilogue)
+    cur_t = nxt_t;
+    pair_base = (pair_base + static_cast<uint32_t>(KP)) % 3u;
+    start_tile(cur, slot_of(0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
   }
 }
 
 
 // Launch of one variant: OUT 0 fp32 C, 1 bf16 C, 2 NVFP4 C; the pipelined kernel for whole K steps
-// (full), with block scales two steps per load (paired), else the bounds-checked kernel.
+// (full), with block scales two steps per load (paired), else the bounds-checked kernel.  grid:
+// workgroups (p.total_tiles, or fewer for the pipelined kernel with bf16 C and at least four K
+// steps, whose workgroups then run several tiles each).
 template <int OUT, bool A2D, bool B2D>
-hipError_t launch_variant(const GemmKArgs &p, int32_t tiles, bool full, bool paired, hipStream_t stream) {
+hipError_t launch_variant(const GemmKArgs &p, int32_t grid, bool full, bool paired, hipStream_t stream) {
   if (paired)
-    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if constexpr (OUT == 2)
     return hipErrorInvalidValue;  // the quantized epilogue exists in the paired kernel only
   else if (full)
-    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<OUT == 1, A2D, B2D, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<OUT == 1, A2D, B2D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -76,7 +76,9 @@ __device__ __forceinline__ void write_tile(const floatx16 (&acc)[4][4], float *c
 // (256: one wave per SIMD; 512: two, which a 2 x 4 tile's 128 accumulators allow).
 // DECODE: 1 = each use decodes its operands (the library's K loop), 0 = the MFMAs alone on operands
 // decoded once, 2 = the MFMAs on operands decoded once plus the same decode work on other registers
-// (independent of the MFMAs: whether a wave's VALU work overlaps its own MFMAs at all).
+// (independent of the MFMAs: whether a wave's VALU work overlaps its own MFMAs at all), 3 = as 2 with
+// conversions only (eight independent v_cvt per 8 codes instead of four conversions and four
+// multiplies that depend on them).
 template <int TM, int TN, int DECODE, int NT>
 __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
   const uint32_t lane = threadIdx.x & 63u, l32 = lane & 31u, h = lane >> 5;
@@ -108,8 +110,27 @@ __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
 #pragma unroll
   for (int f = 0; f < TN; ++f) bf[f] = decode8(cb[f], sb[f]);
   for (int rep = 0; rep < p.reps; ++rep) {
-    half8 ta[TM], tb[TN];  // DECODE == 2: decoded values that no MFMA reads
-    if constexpr (DECODE == 2) {
+    half8 ta[TM], tb[TN];  // DECODE == 2, 3: decoded values that no MFMA reads
+    if constexpr (DECODE == 3) {
+      auto cvt8 = [](uint32_t w) {
+        const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+        const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+        const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+        const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+        const half2v q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 0);
+        const half2v q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 1);
+        const half2v q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 2);
+        const half2v q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 3);
+        half8 r0 = half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        half8 r1 = half8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+        opaque(r1);
+        return r0;
+      };
+#pragma unroll
+      for (int f = 0; f < TM; ++f) ta[f] = cvt8(ca[f] ^ static_cast<uint32_t>(rep));
+#pragma unroll
+      for (int f = 0; f < TN; ++f) tb[f] = cvt8(cb[f] ^ static_cast<uint32_t>(rep));
+    } else if constexpr (DECODE == 2) {
       // codes that change with the repetition (one v_xor), so the decode cannot be hoisted
 #pragma unroll
       for (int f = 0; f < TM; ++f) ta[f] = decode8(ca[f] ^ static_cast<uint32_t>(rep), sa[f]);
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(NT, 1) void probe_fp16_decode(ProbeArgs p) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    if constexpr (DECODE == 2) {
+    if constexpr (DECODE >= 2) {
       // one MFMA, then its share of the decode instructions, throughout
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
@@ -260,7 +281,8 @@ __global__ __launch_bounds__(256, 1) void probe_fp4_rescale(ProbeArgs p) {
 // design 0 alone (operands decoded once: the cost of the decode is the difference); on a 2 x 4 wave
 // tile (64 x 128): 3 = design 0 with two waves per SIMD, 4 = design 0 with one, 5 = design 2 with
 // two; 6 = design 2 plus design 0's decode work on registers the MFMAs do not read (4 x 4 tile, one
-// wave per SIMD); 7 = design 0 software-pipelined (4 x 4 tile, one wave per SIMD).  Designs 0-2 and 6 run workgroups of 4 waves (one per SIMD), 3-5 of 8 or 4; every
+// wave per SIMD); 7 = design 0 software-pipelined (4 x 4 tile, one wave per SIMD); 8 = design 6 with
+// conversions only (no VALU instruction waits for another).  Designs 0-2 and 6 run workgroups of 4 waves (one per SIMD), 3-5 of 8 or 4; every
 // wave runs the same step; returns 0, or the HIP error code of the launch.
 extern "C" __attribute__((visibility("default"))) int nvfp4_probe_design(int design, const uint8_t *a_codes,
                                                                          const uint8_t *a_scales, const uint8_t *b_codes,
@@ -285,6 +307,8 @@ extern "C" __attribute__((visibility("default"))) int nvfp4_probe_design(int des
     hipLaunchKernelGGL((probe_fp16_decode<4, 4, 2, 256>), dim3(workgroups), dim3(256), 0, st, p);
   else if (design == 7)
     hipLaunchKernelGGL(probe_fp16_pipelined, dim3(workgroups), dim3(256), 0, st, p);
+  else if (design == 8)
+    hipLaunchKernelGGL((probe_fp16_decode<4, 4, 3, 256>), dim3(workgroups), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(probe_fp4_rescale, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
