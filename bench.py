@@ -67,15 +67,16 @@ def gemm_source_digest():
     """sha256 over the GEMM kernel sources (the counters below are only valid for this source)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_common.hpp", "nvfp4_device.hpp"):
+    for f in ("gemm.hip", "gemm_kernels.hpp", "gemm_variant.hip", "gemm_common.hpp", "nvfp4_device.hpp"):
         with open(os.path.join(ROOT, "nvfp4_bit_block_quantize_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_gemm_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled
-    by the copy-kernel calibration; None when the summary is missing or was taken on other sources."""
+def measured_gemm_counters():
+    """The committed rocprofv3 counter summary of the GEMM (profiles/gemm_fprop8b_traffic.json: HBM
+    bytes per launch from FETCH_SIZE / WRITE_SIZE scaled by the copy-kernel calibration, MFMA busy
+    fraction and shader clock); None when it is missing or was taken on other sources."""
     path = os.path.join(ROOT, "profiles", "gemm_fprop8b_traffic.json")
     try:
         with open(path) as fh:
@@ -84,7 +85,7 @@ def measured_gemm_traffic():
         return None
     if t.get("gemm_source_sha256") != gemm_source_digest():
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t
 
 
 def _counter_per_dispatch(csv_path, name_part, counter):
@@ -101,6 +102,28 @@ def _counter_per_dispatch(csv_path, name_part, counter):
     return sum(per.values()) / len(per), len(per)
 
 
+def _mfma_per_dispatch(csv_path, name_part):
+    """Per dispatch of kernels whose name contains name_part: MFMA busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), shader clock
+    (GRBM_GUI_ACTIVE / 8 over the dispatch's duration) and VALU instructions per MFMA."""
+    import csv
+    per, span = {}, {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if name_part not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            span[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = []
+    for k, c in per.items():
+        g = c["GRBM_GUI_ACTIVE"] / 8
+        out.append((c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024), g / span[k], c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] - 1))
+    if not out:
+        raise SystemExit(f"no counter rows for '{name_part}' in {csv_path}")
+    return out
+
+
 def traffic_summary(d):
     copy_kib = 1024 * 1024  # --copy-calibration 1024: 1 GiB read and 1 GiB written per launch
     cf, _ = _counter_per_dispatch(os.path.join(d, "cpy_FETCH_SIZE", "p_counter_collection.csv"), "copyBuffer", "FETCH_SIZE")
@@ -108,17 +131,28 @@ def traffic_summary(d):
     gf, nf = _counter_per_dispatch(os.path.join(d, "pmc_FETCH_SIZE", "p_counter_collection.csv"), "gemm", "FETCH_SIZE")
     gw, nw = _counter_per_dispatch(os.path.join(d, "pmc_WRITE_SIZE", "p_counter_collection.csv"), "gemm", "WRITE_SIZE")
     fs, ws = copy_kib / cf, copy_kib / cw
+    # MFMA pass: the dispatches after the first few (clocks settle over the warm-up)
+    mf = _mfma_per_dispatch(os.path.join(d, "pmc_MFMA", "p_counter_collection.csv"), "gemm")
+    mf = mf[len(mf) // 2:]
     M, N, K = 8192, 14336, 4096
     cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $OUT/{d} -o p -- python3 $REPO/bench.py {a}"
     out = {
         "what": "HBM-side traffic per launch of the NVFP4 GEMM (fprop 8192x14336x4096, bf16 out), from rocprofv3 "
                 "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the dispatches), each scaled by the "
-                "same counter's reading for a device-to-device copy of 1024 MiB",
+                "same counter's reading for a device-to-device copy of 1024 MiB; and the MFMA busy fraction "
+                "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)) at the shader clock "
+                "(GRBM_GUI_ACTIVE / 8 over the dispatch's duration), over the later half of the dispatches",
         "commands": [cmd.format(c="FETCH_SIZE", d="pmc_FETCH_SIZE", a="--steps 2 --warmup 1 --no-cpu"),
                      cmd.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", a="--steps 2 --warmup 1 --no-cpu"),
                      cmd.format(c="FETCH_SIZE", d="cpy_FETCH_SIZE", a="--copy-calibration 1024"),
                      cmd.format(c="WRITE_SIZE", d="cpy_WRITE_SIZE", a="--copy-calibration 1024"),
+                     cmd.format(c="SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU GRBM_GUI_ACTIVE", d="pmc_MFMA",
+                                a="--steps 10 --warmup 5 --no-cpu"),
                      "python3 bench.py --traffic-summary $OUT"],
+        "mfma_busy_frac": round(sum(x[0] for x in mf) / len(mf), 4),
+        "sclk_ghz": round(sum(x[1] for x in mf) / len(mf), 3),
+        "valu_per_mfma": round(sum(x[2] for x in mf) / len(mf), 3),
+        "mfma_dispatches": len(mf),
         "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1), "copy_true_kib_each_way": copy_kib,
         "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
         "gemm_dispatches": [nf, nw],
@@ -377,6 +411,7 @@ def main():
     w4_bytes = M * K * 2 + N * K // 2 + N * K // 256 + M * N * 2
     value = flops / (ms_step * 1e-3) / 1e12
 
+    counters = measured_gemm_counters() if a.workload == "fprop8b" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -392,9 +427,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "M": M, "N": N, "K": K, "out": str(out_dtype).replace("torch.", "")},
         "components": {
-            "quantize_gbps": round(quant_gbps, 1),
-            "quantize_hbm_frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
+            "quantize_warm_gbps": round(quant_gbps, 1),
             "quantize_cold_gbps": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9, 1) if qbytes else None,
+            # (the cold rate: inputs flushed from the Infinity Cache, as a training step meets them)
+            "quantize_hbm_frac": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if qbytes else None,
             "copy_ceiling_gbps": round(copy_gbps, 1),
             "quantize_frac_of_copy": round(quant_gbps / copy_gbps, 4) if qbytes else None,
             "quantize_cold_a_ms": round(qa_cold, 4),
@@ -413,9 +449,15 @@ def main():
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
-            "traffic": measured_gemm_traffic() if a.workload == "fprop8b" else None,
+            "traffic": counters.get("traffic_bytes_per_launch") if counters else None,
         },
     }
+    if counters:
+        # MFMA busy fraction and shader clock of the committed counter run of this source: the
+        # peak at that clock is 2.5 PFLOP/s x sclk / 2.4 GHz
+        sclk = counters["sclk_ghz"]
+        result["roofline"].update({"mfma_busy": counters["mfma_busy_frac"], "sclk_ghz": sclk,
+                                   "frac_at_sclk": round(gemm_tflops / (PEAK_F16_TFLOPS * sclk / 2.4), 4)})
     if fused:
         result["components"]["unfused_gemm_bf16_plus_quantize_ms"] = round(unfused_ms, 4)
         result["components"]["step_timing"] = ("HIP graph replay of quantize(A) + quantize(B) + tensor scale from "
