@@ -45,7 +45,7 @@ def _args():
                             "fprop405b", "moe", "dequant8b", "gemm_designs"])
     p.add_argument("--decode-tokens", type=int, default=16, help="rows of X in the w4a16_decode workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=2048, help="rows of X and W in the CPU sample")
+    p.add_argument("--cpu-rows", type=int, default=8192, help="rows of X and W in the CPU sample (about 10 s on 16 cores)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run 5 device-to-device copies of MIB MiB (a known-size kernel for scaling "
                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
