@@ -155,6 +155,40 @@ __device__ __forceinline__ uint32_t pack8_sr(const float *y, float e, const u32x
   return even | (odd << 4);
 }
 
+// ~(w << 16), the random operand of an even element (r16 = low half of w), in one instruction:
+// sign-extended low 24 bits of w times -2^16 is -(w << 16) modulo 2^32, minus 1 is its complement.
+__device__ __forceinline__ uint32_t seed_low_half(uint32_t w) {
+  uint32_t r;
+  asm("v_mad_i32_i24 %0, %1, %2, -1" : "=v"(r) : "v"(w), "s"(-65536));
+  return r;
+}
+
+// Stochastic rounding with the 2^23 pre-scale folded into the block factor: the instruction's
+// operand is ceil(RN(|y| * E)) with the sign of y, E = e * 2^23, or E = e * 2^21 when y holds four
+// times the values to encode (the Hadamard transform's 1/4 left out).  encode_block_sr states when
+// this equals the operand of sr_elem.
+template <int T>  // element T of 8; w = its Philox word
+__device__ __forceinline__ void sr_elem_folded(float y, float E, uint32_t w, uint32_t &even, uint32_t &odd) {
+  const float xs = __builtin_copysignf(__builtin_ceilf(fabsf(y) * E), y);
+  if constexpr ((T & 1) != 0)
+    odd = cvt_sr_byte<(T >> 1)>(odd, xs, ~w | 0xFFFFu);
+  else
+    even = cvt_sr_byte<(T >> 1)>(even, xs, seed_low_half(w));
+}
+
+__device__ __forceinline__ uint32_t pack8_sr_folded(const float *y, float E, const u32x4 &w) {
+  uint32_t even = 0u, odd = 0u;
+  sr_elem_folded<0>(y[0], E, w.x, even, odd);
+  sr_elem_folded<1>(y[1], E, w.x, even, odd);
+  sr_elem_folded<2>(y[2], E, w.y, even, odd);
+  sr_elem_folded<3>(y[3], E, w.y, even, odd);
+  sr_elem_folded<4>(y[4], E, w.z, even, odd);
+  sr_elem_folded<5>(y[5], E, w.z, even, odd);
+  sr_elem_folded<6>(y[6], E, w.w, even, odd);
+  sr_elem_folded<7>(y[7], E, w.w, even, odd);
+  return even | (odd << 4);
+}
+
 // Decoded error terms of one byte of packed codes (two elements, low nibble first) under scale S:
 // the decoded value is RN(RN(q * S) * ts), where q * S is exact (q has at most two significant bits,
 // S four, and the product stays normal).  v_cvt_scalef32_pk_f32_fp4 with scale 1.0 returns the two
@@ -208,6 +242,113 @@ __device__ __forceinline__ float block_sse(const float (&y)[16], uint32_t w0, ui
   return sse_pair<3>(w1, y[14], y[15], S, ts, acc);
 }
 
+// ---- stochastic rounding: per-workgroup tables and reciprocal divisions ---------------------------
+// RN(a / b) from y = RN(1 / b): q = RN(a y) is within two ulps of a / b; one residual correction
+// (r = a - q b by fma) makes it faithful, and a second one, whose residual is then exact, gives
+// the correctly rounded quotient (Markstein's theorem: y within half an ulp of 1 / b, q within one
+// ulp of a / b).  Valid while a, b, the quotient and the residuals are normal: the callers keep
+// a in [2^-90, 2^100] (or 0) and b in [2^-100, 2^100].  Checked against IEEE division on the CPU
+// for b = 6 and every a in [2^-90, 2^100], and for 2000 random b with 10^6 a each.
+__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
+  float q = a * y;
+  float r = fmaf(-q, b, a);
+  q = fmaf(r, y, q);
+  r = fmaf(-q, b, a);
+  return fmaf(r, y, q);
+}
+
+constexpr float kRecip6 = 0x1.555556p-3f;  // RN(1 / 6)
+
+// Scale byte of a block with maximum ab (target 6), as block_scale computes it.  With ts in
+// [2^-100, 2^100] (recip_ok; yts = RN(1 / ts)) and ab = 0 or in [2^-90, 2^100], both divisions go
+// through div_by_recip: RN(ab / 6) is then normal, and RN(q / ts) is correctly rounded wherever it
+// is normal; where it is not (below 2^-126) both forms are far below 2^-10, the smallest value
+// that rounds to a nonzero scale, so the byte is 0 either way.
+__device__ __forceinline__ uint32_t block_scale_byte(float ab, float ts, float yts, bool recip_ok) {
+  float S;
+  if (recip_ok && (ab == 0.0f || (ab >= 0x1p-90f && ab <= 0x1p100f))) {
+    const float q = div_by_recip(ab, 6.0f, kRecip6);
+    const float sc = fminf(div_by_recip(q, ts, yts), 448.0f);
+    return e4m3_rne(sc, S);
+  }
+  return block_scale(ab, 6.0f, ts, S);
+}
+
+// Per-workgroup tables of the 127 scale bytes a block can get (s <= 448 rounds to at most 0x7E):
+// e[b] = encode_factor(S(b), ts), and E[b] = e[b] * FOLD where the folded stochastic rounding
+// applies to that factor (encode_block_sr), else -1.
+struct SrTables {
+  float e[128];
+  float E[128];
+};
+
+template <int ESZ, bool QUARTER>
+__device__ __forceinline__ void build_sr_tables(SrTables &t, float ts) {
+  if (threadIdx.x < 128) {
+    const uint32_t b = threadIdx.x;
+    const float S = b < 8 ? static_cast<float>(b) * 0.001953125f
+                          : __uint_as_float((((b >> 3) + 120u) << 23) | ((b & 7u) << 20));
+    const float e = encode_factor(S, ts);
+    constexpr float kMinFactor = ESZ == 2 ? 0x1p-14f : 1.0f;
+    const bool fold = e == 0.0f || (e >= kMinFactor && e <= 0x1p100f);
+    t.e[b] = e;
+    t.E[b] = fold ? e * (QUARTER ? 0x1p21f : 0x1p23f) : -1.0f;
+  }
+  __syncthreads();
+}
+
+// Stochastic-rounding encode of one 1D block of y' = y (QUARTER: y' = y / 4, y the Hadamard
+// transform without its 1/4), as encode_block<kSR> of y'.  With v = RN(|y'| e), sr_elem feeds the
+// instruction ceil(RN(v * 2^23)); the folded form feeds ceil(RN(|y'| e 2^23)), one rounding of the
+// same product scaled by a power of two.  The two agree
+//   - where v is normal: scaling by 2^23 commutes with rounding;
+//   - where v is subnormal or zero: both operands are below 1 before the ceil, so both are 1 for a
+//     product that rounds to a nonzero value and 0 otherwise, and the two products round to zero
+//     together as long as |y'| e > 2^-150 for every nonzero y'.  Nonzero bf16 values, and the
+//     quarters of their transforms, are at least 2^-135 (multiples of 2^-135: the inputs are
+//     multiples of 2^-133 and so are all fp32 sums and differences of them), so e >= 2^-14 suffices;
+//     nonzero fp32 values are at least 2^-149, so e >= 1 (no fold of the quarter: y / 4 may round);
+//   - for e = 0 (a zero block scale): both are 0 (y' finite) or the same NaN;
+//   - and E = e 2^23 stays finite for e <= 2^100.
+// Other factors (inf: S * ts underflowed; NaN) take the unfolded path.  The factor of each scale
+// byte, and whether it folds, come from the workgroup's tables (build_sr_tables).
+template <int ESZ, bool QUARTER>
+__device__ __forceinline__ void encode_block_sr(const float (&y)[16], float ts, float yts, bool recip_ok,
+                                                const SrTables &tab, uint64_t i0, uint32_t key0, uint32_t key1,
+                                                uint32_t stream_id, uint32_t &sbyte, uint32_t &w0, uint32_t &w1) {
+  static_assert(ESZ == 2 || !QUARTER, "the quarter of an fp32 transform may round");
+  float ab = block_absmax(y);
+  if constexpr (QUARTER) ab = ab * 0.25f;  // = max RN(|y| / 4): rounding is monotone
+  sbyte = block_scale_byte(ab, ts, yts, recip_ok);
+  const float E = tab.E[sbyte];
+  const uint64_t call = i0 >> 3;
+  const u32x4 r0 = philox4x32_10(static_cast<uint32_t>(call), static_cast<uint32_t>(call >> 32), stream_id, 0u,
+                                 key0, key1);
+  const u32x4 r1 = philox4x32_10(static_cast<uint32_t>(call + 1), static_cast<uint32_t>((call + 1) >> 32),
+                                 stream_id, 0u, key0, key1);
+  if (E >= 0.0f) {
+    w0 = pack8_sr_folded(y, E, r0);
+    w1 = pack8_sr_folded(y + 8, E, r1);
+  } else {
+    const float e = tab.e[sbyte];
+    float yq[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) yq[t] = QUARTER ? y[t] * 0.25f : y[t];
+    if (__builtin_isinf(e)) {
+      w0 = 0u;
+      w1 = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        w0 |= code_degenerate(yq[t]) << (4 * t);
+        w1 |= code_degenerate(yq[8 + t]) << (4 * t);
+      }
+    } else {
+      w0 = pack8_sr(yq, e, r0);
+      w1 = pack8_sr(yq + 8, e, r1);
+    }
+  }
+}
+
 // Full encode of one 1D block: scale byte and two packed words (nibble t at bits 4t).  With
 // Four-over-Six (targets 6, 4) or the scale search (6, 5.5, 5, 4.5, 4) every target gives a scale
 // and codes; the block keeps the lowest squared error, a later target only if strictly lower.
@@ -253,6 +394,11 @@ __device__ __forceinline__ void write_partial(uint32_t m, uint32_t *__restrict__
     partial[blockIdx.x] = r;
   }
 }
+
+// The maximum of RN(|u| / 4) over values whose largest |u| has the float bits m: rounding is
+// monotone, so the maximum of the quartered values is the quartered maximum (pass 1 of the Hadamard
+// variants takes the 1/4 of the transform once per lane instead of once per element).
+__device__ __forceinline__ uint32_t quarter_bits(uint32_t m) { return __float_as_uint(__uint_as_float(m) * 0.25f); }
 
 // Tensor amax from the pass-1 partial maxima (float bits of non-negative values compare like
 // unsigned integers), reduced by every wave on its own (at most kPass1Parts values, no barrier);
@@ -372,13 +518,23 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   if (b < p.nblocks) cur = load_raw16<ESZ>(src(b));
   float ts = 0.0f;
   if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
+  // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
+  constexpr bool QUARTER = RHT && (PASS1 || (MODE == kSR && ESZ == 2));
+  __shared__ SrTables tab;
+  float yts = 0.0f;
+  bool recip_ok = false;
+  if constexpr (MODE == kSR && !PASS1) {
+    build_sr_tables<ESZ, QUARTER>(tab, ts);
+    recip_ok = ts >= 0x1p-100f && ts <= 0x1p100f;
+    yts = 1.0f / ts;
+  }
   uint32_t mx = 0;
   while (b < p.nblocks) {
     const uint32_t bn = b + stride;
     if (bn < p.nblocks) nxt = load_raw16<ESZ>(src(bn));
     float y[16];
     unpack16<ESZ>(cur, y);
-    if constexpr (RHT) rht16(y, p.sign_word);
+    if constexpr (RHT) rht16<!QUARTER>(y, p.sign_word);
     if constexpr (PASS1) {
       mx = max(mx, __float_as_uint(block_absmax(y)));
     } else {
@@ -386,20 +542,25 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
       const uint64_t i0 = static_cast<uint64_t>(r) * static_cast<uint64_t>(p.K) + 16u * (b - r * p.kb.d);
       if constexpr (RHT) {
         if (p.rht_out) {
+          const float f = QUARTER ? 0.25f : 1.0f;
           float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+          for (int q = 0; q < 4; ++q)
+            o[q] = make_float4(y[4 * q] * f, y[4 * q + 1] * f, y[4 * q + 2] * f, y[4 * q + 3] * f);
         }
       }
       uint32_t sb, w0, w1;
-      encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+      if constexpr (MODE == kSR)
+        encode_block_sr<ESZ, QUARTER>(y, ts, yts, recip_ok, tab, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+      else
+        encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       *reinterpret_cast<uint2 *>(p.data + (i0 >> 1)) = make_uint2(w0, w1);
       p.scales[i0 >> 4] = static_cast<uint8_t>(sb);
     }
     cur = nxt;
     b = bn;
   }
-  if constexpr (PASS1) write_partial(mx, p.partial_out);
+  if constexpr (PASS1) write_partial(RHT ? quarter_bits(mx) : mx, p.partial_out);
 }
 
 // Nearest-even codes of 8 values under factor e (e = +inf: S * ts underflowed, see code_degenerate).
@@ -625,19 +786,36 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   }
   float ts = 0.0f;
   if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
+  // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
+  constexpr bool QUARTER = RHT && MODE == kSR && ESZ == 2;
+  __shared__ SrTables tab;
+  float yts = 0.0f;
+  bool recip_ok = false;
+  if constexpr (MODE == kSR && !PASS1) {
+    build_sr_tables<ESZ, QUARTER>(tab, ts);
+    recip_ok = ts >= 0x1p-100f && ts <= 0x1p100f;
+    yts = 1.0f / ts;
+  }
   for (; tile < p.ntiles; tile += gridDim.x) {
     if constexpr (PASS1) {
+      // the next tile's loads go out before this tile's maxima
+      Raw8<ESZ> vn[16];
+      const bool more = tile + gridDim.x < p.ntiles;
+      if (more) {
+        locate(tile + gridDim.x);
+        load_patch<ESZ>(vn, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         float u[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) u[t] = raw8_elem<ESZ>(v[t], c);
-        if constexpr (RHT) rht16(u, p.sign_word);
+        if constexpr (RHT) rht16<false>(u, p.sign_word);
         mx = max(mx, __float_as_uint(block_absmax(u)));
       }
-      if (tile + gridDim.x < p.ntiles) {
-        locate(tile + gridDim.x);
-        load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[t] = vn[t];
       }
       continue;
     }
@@ -673,19 +851,23 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       float u[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) u[t] = raw8_elem<ESZ>(v[t], c);
-      if constexpr (RHT) rht16(u, p.sign_word);
+      if constexpr (RHT) rht16<!QUARTER>(u, p.sign_word);
       const uint64_t i0 = static_cast<uint64_t>(rr + c) * static_cast<uint64_t>(p.K) + static_cast<uint64_t>(kk);
       if constexpr (RHT) {
         if (p.rht_out && valid) {
+          const float f = QUARTER ? 0.25f : 1.0f;
           float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = make_float4(u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]);
+          for (int q = 0; q < 4; ++q)
+            o[q] = make_float4(u[4 * q] * f, u[4 * q + 1] * f, u[4 * q + 2] * f, u[4 * q + 3] * f);
         }
       }
       uint32_t sb, w0, w1;
       if constexpr (B2D) {
         block_words<kRNE>(u, e2d, i0, 0u, 0u, 0u, w0, w1);
         sb = sb2d;
+      } else if constexpr (MODE == kSR) {
+        encode_block_sr<ESZ, QUARTER>(u, ts, yts, recip_ok, tab, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       } else {
         encode_block<MODE>(u, block_absmax(u), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       }
@@ -741,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     }
     __syncthreads();
   }
-  if constexpr (PASS1) write_partial(mx, p.partial_out);
+  if constexpr (PASS1) write_partial(RHT ? quarter_bits(mx) : mx, p.partial_out);
 }
 
 __global__ void zero_ts_kernel(float *ts, uint32_t n) {
@@ -752,6 +934,29 @@ __global__ void zero_ts_kernel(float *ts, uint32_t n) {
 uint32_t clamp_grid(uint64_t want, uint64_t cap) {
   if (want < 1) want = 1;
   return static_cast<uint32_t>(want < cap ? want : cap);
+}
+
+// Workgroups of kThreads threads of `kernel` that the current device holds at once (0 if unknown),
+// cached per kernel and device.
+uint32_t resident_groups(const void *kernel) {
+  struct Entry {
+    const void *k;
+    int dev;
+    uint32_t n;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].n;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess)
+    return 0;
+  const uint32_t n = static_cast<uint32_t>(cus) * static_cast<uint32_t>(per);
+  if (used < 64) cache[used++] = Entry{kernel, dev, n};
+  return n;
 }
 
 template <int ESZ>
@@ -799,7 +1004,11 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kPass1Parts);
     hipLaunchKernelGGL((row1d_kernel<ESZ, kRNE, true, true>), dim3(nparts, G), dim3(kThreads), 0, a.stream, ra);
   } else {
-    nparts = clamp_grid(col_tiles, kPass1Parts);
+    // one round of resident workgroups: a second, partial round would run at a fraction of the
+    // machine's bandwidth
+    const void *k1 = reinterpret_cast<const void *>(&col_kernel<ESZ, kRNE, true, false, true, false>);
+    const uint32_t res = resident_groups(k1);
+    nparts = clamp_grid(col_tiles, res > 0 && res < kPass1Parts ? res : kPass1Parts);
     hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false>), dim3(nparts, G), dim3(kThreads), 0, a.stream, ca);
   }
   hipError_t err = hipGetLastError();
