@@ -23,6 +23,8 @@
 //                  x^T; a 256-lane workgroup covers 256 tokens x 128 columns and transposes its
 //                  packed output through LDS so that every row segment leaves as 128 contiguous
 //                  bytes.
+#include <type_traits>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.h"
 
@@ -70,30 +72,84 @@ __device__ __forceinline__ void unpack16(const Raw16<ESZ> &r, float (&y)[16]) {
   }
 }
 
-// 8 consecutive elements at p (16 B bf16 / 32 B f32) kept raw.
+// unpack16 with the Hadamard transform's random signs applied (bit t of sign_word flips element t);
+// the low bf16 half takes its flip as an addition of 2^31 (see rawn_elem_signed).
 template <int ESZ>
-struct Raw8 {
-  uint4 v[ESZ / 2];
-};
-
-template <int ESZ>
-__device__ __forceinline__ Raw8<ESZ> load8(const uint8_t *__restrict__ p) {
-  Raw8<ESZ> r;
+__device__ __forceinline__ void unpack16_signed(const Raw16<ESZ> &r, float (&y)[16], uint32_t sign_word) {
 #pragma unroll
-  for (int i = 0; i < ESZ / 2; ++i) r.v[i] = *reinterpret_cast<const uint4 *>(p + 16 * i);
+  for (int i = 0; i < ESZ; ++i) {
+    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (ESZ == 2) {
+        const int t = 8 * i + 2 * j;
+        y[t] = __uint_as_float((w[j] << 16) + (((sign_word >> t) & 1u) << 31));
+        y[t + 1] = __uint_as_float((w[j] & 0xFFFF0000u) ^ (((sign_word >> (t + 1)) & 1u) << 31));
+      } else {
+        const int t = 4 * i + j;
+        y[t] = __uint_as_float(w[j] ^ (((sign_word >> t) & 1u) << 31));
+      }
+    }
+  }
+}
+
+// N consecutive elements at p (2N bytes of bf16 / 4N of f32, N = 4 or 8) kept raw, loaded 8 or 16
+// bytes at a time.
+template <int ESZ, int N = 8>
+struct RawN {
+  static constexpr int kBytes = N * ESZ;
+  typedef typename std::conditional<kBytes == 8, uint2, uint4>::type Vec;
+  Vec v[kBytes >= 16 ? kBytes / 16 : 1];
+};
+template <int ESZ>
+using Raw8 = RawN<ESZ, 8>;
+
+template <int ESZ, int N = 8>
+__device__ __forceinline__ RawN<ESZ, N> loadn(const uint8_t *__restrict__ p) {
+  RawN<ESZ, N> r;
+  typedef typename RawN<ESZ, N>::Vec Vec;
+#pragma unroll
+  for (int i = 0; i < (N * ESZ >= 16 ? N * ESZ / 16 : 1); ++i) r.v[i] = *reinterpret_cast<const Vec *>(p + 16 * i);
   return r;
+}
+
+// 32-bit word q of a raw group (constant q after unrolling)
+template <int ESZ, int N>
+__device__ __forceinline__ uint32_t rawn_word(const RawN<ESZ, N> &r, int q) {
+  if constexpr (N * ESZ == 8) {
+    return q == 0 ? r.v[0].x : r.v[0].y;
+  } else {
+    const uint4 &x = r.v[q >> 2];
+    return (q & 3) == 0 ? x.x : (q & 3) == 1 ? x.y : (q & 3) == 2 ? x.z : x.w;
+  }
+}
+
+template <int ESZ, int N = 8>
+__device__ __forceinline__ float rawn_elem(const RawN<ESZ, N> &r, int c) {
+  if constexpr (ESZ == 2) {
+    const uint32_t w = rawn_word<ESZ, N>(r, c >> 1);
+    return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    return __uint_as_float(rawn_word<ESZ, N>(r, c));
+  }
+}
+
+// Element c with its sign flipped when sflip (0 or 2^31) is set: the random signs D of the Hadamard
+// transform applied while unpacking.  For the low bf16 half, adding 2^31 to w << 16 flips its top
+// bit (the carry leaves the word), one shift-and-add instead of a shift and an exclusive or.
+template <int ESZ, int N>
+__device__ __forceinline__ float rawn_elem_signed(const RawN<ESZ, N> &r, int c, uint32_t sflip) {
+  if constexpr (ESZ == 2) {
+    const uint32_t w = rawn_word<ESZ, N>(r, c >> 1);
+    return (c & 1) ? __uint_as_float((w & 0xFFFF0000u) ^ sflip) : __uint_as_float((w << 16) + sflip);
+  } else {
+    return __uint_as_float(rawn_word<ESZ, N>(r, c) ^ sflip);
+  }
 }
 
 template <int ESZ>
 __device__ __forceinline__ float raw8_elem(const Raw8<ESZ> &r, int c) {
-  if constexpr (ESZ == 2) {
-    uint32_t w = (c >> 1) == 0 ? r.v[0].x : (c >> 1) == 1 ? r.v[0].y : (c >> 1) == 2 ? r.v[0].z : r.v[0].w;
-    return (c & 1) ? bf16_hi(w) : bf16_lo(w);
-  } else {
-    const uint4 &q = r.v[c >> 2];
-    uint32_t w = (c & 3) == 0 ? q.x : (c & 3) == 1 ? q.y : (c & 3) == 2 ? q.z : q.w;
-    return __uint_as_float(w);
-  }
+  return rawn_elem<ESZ, 8>(r, c);
 }
 
 // ---- element codes --------------------------------------------------------------------------------
@@ -313,7 +369,7 @@ __device__ __forceinline__ void build_sr_tables(SrTables &t, float ts) {
 // Other factors (inf: S * ts underflowed; NaN) take the unfolded path.  The factor of each scale
 // byte, and whether it folds, come from the workgroup's tables (build_sr_tables).
 template <int ESZ, bool QUARTER>
-__device__ __forceinline__ void encode_block_sr(const float (&y)[16], float ts, float yts, bool recip_ok,
+__device__ __forceinline__ void encode_block_sr(float (&y)[16], float ts, float yts, bool recip_ok,
                                                 const SrTables &tab, uint64_t i0, uint32_t key0, uint32_t key1,
                                                 uint32_t stream_id, uint32_t &sbyte, uint32_t &w0, uint32_t &w1) {
   static_assert(ESZ == 2 || !QUARTER, "the quarter of an fp32 transform may round");
@@ -331,20 +387,21 @@ __device__ __forceinline__ void encode_block_sr(const float (&y)[16], float ts, 
     w1 = pack8_sr_folded(y + 8, E, r1);
   } else {
     const float e = tab.e[sbyte];
-    float yq[16];
+    if constexpr (QUARTER) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) yq[t] = QUARTER ? y[t] * 0.25f : y[t];
+      for (int t = 0; t < 16; ++t) y[t] = y[t] * 0.25f;  // in place: y is not read after the encode
+    }
     if (__builtin_isinf(e)) {
       w0 = 0u;
       w1 = 0u;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        w0 |= code_degenerate(yq[t]) << (4 * t);
-        w1 |= code_degenerate(yq[8 + t]) << (4 * t);
+        w0 |= code_degenerate(y[t]) << (4 * t);
+        w1 |= code_degenerate(y[8 + t]) << (4 * t);
       }
     } else {
-      w0 = pack8_sr(yq, e, r0);
-      w1 = pack8_sr(yq + 8, e, r1);
+      w0 = pack8_sr(y, e, r0);
+      w1 = pack8_sr(y + 8, e, r1);
     }
   }
 }
@@ -533,8 +590,12 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
     const uint32_t bn = b + stride;
     if (bn < p.nblocks) nxt = load_raw16<ESZ>(src(bn));
     float y[16];
-    unpack16<ESZ>(cur, y);
-    if constexpr (RHT) rht16<!QUARTER>(y, p.sign_word);
+    if constexpr (RHT) {
+      unpack16_signed<ESZ>(cur, y, p.sign_word);
+      rht16_butterfly<!QUARTER>(y);
+    } else {
+      unpack16<ESZ>(cur, y);
+    }
     if constexpr (PASS1) {
       mx = max(mx, __float_as_uint(block_absmax(y)));
     } else {
@@ -542,11 +603,17 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
       const uint64_t i0 = static_cast<uint64_t>(r) * static_cast<uint64_t>(p.K) + 16u * (b - r * p.kb.d);
       if constexpr (RHT) {
         if (p.rht_out) {
-          const float f = QUARTER ? 0.25f : 1.0f;
           float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
+          float w[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            o[q] = make_float4(y[4 * q] * f, y[4 * q + 1] * f, y[4 * q + 2] * f, y[4 * q + 3] * f);
+          for (int t = 0; t < 16; ++t) {
+            // opaque copy: the quarters stay in this branch (not hoisted as common with the encode's)
+            w[t] = y[t];
+            asm volatile("" : "+v"(w[t]));
+            if constexpr (QUARTER) w[t] = w[t] * 0.25f;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
         }
       }
       uint32_t sb, w0, w1;
@@ -590,16 +657,16 @@ struct Row2dArgs {
   GroupStrides g;
 };
 
-template <int ESZ>
-__device__ __forceinline__ void load_patch(Raw8<ESZ> (&v)[16], const uint8_t *__restrict__ base, int64_t ld_bytes,
+template <int ESZ, int N = 8>
+__device__ __forceinline__ void load_patch(RawN<ESZ, N> (&v)[16], const uint8_t *__restrict__ base, int64_t ld_bytes,
                                            bool valid) {
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     if (valid) {
-      v[t] = load8<ESZ>(base + t * ld_bytes);
+      v[t] = loadn<ESZ, N>(base + t * ld_bytes);
     } else {
 #pragma unroll
-      for (int i = 0; i < ESZ / 2; ++i) v[t].v[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < (N * ESZ >= 16 ? N * ESZ / 16 : 1); ++i) v[t].v[i] = {};
     }
   }
 }
@@ -755,39 +822,43 @@ struct ColArgs {
 };
 
 constexpr int kColTokens = 256;  // per workgroup tile
-constexpr int kColCols = 128;
 
-template <int ESZ, int MODE, bool RHT, bool B2D, bool PASS1, bool ALIGNED>
+template <int ESZ, int MODE, bool RHT, bool B2D, bool PASS1, bool ALIGNED, int CPL>
 __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
+  static_assert(CPL == 8 || (CPL == 4 && !B2D), "16x16 tiles take a lane pair of 8 columns each");
+  constexpr int COLS = 16 * CPL;  // columns of x (rows of Y) per workgroup tile
   enter_group(p, p.nparts);
   p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   p.stream_id += blockIdx.y;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kColCols * (kColTokens / 2)];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_scales[kColCols * (kColTokens / 16)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS * (kColTokens / 2)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_scales[COLS * (kColTokens / 16)];
   const uint32_t ti = threadIdx.x >> 4;  // token group (16 tokens)
-  const uint32_t tj = threadIdx.x & 15;  // column group (8 columns)
+  const uint32_t tj = threadIdx.x & 15;  // column group (CPL columns)
   const int64_t KB = p.K / 16;
   uint32_t mx = 0;
-  Raw8<ESZ> v[16];
+  RawN<ESZ, CPL> v[16];
   int64_t K0 = 0, R0 = 0, kk = 0, rr = 0;
   bool valid = false;
   auto locate = [&](uint32_t tile) {
     const uint32_t tk = fdiv(tile, p.ntr);
     K0 = static_cast<int64_t>(tk) * kColTokens;
-    R0 = static_cast<int64_t>(tile - tk * p.ntr.d) * kColCols;
+    R0 = static_cast<int64_t>(tile - tk * p.ntr.d) * COLS;
     kk = K0 + 16 * ti;
-    rr = R0 + 8 * tj;
+    rr = R0 + CPL * tj;
     valid = kk < p.K && rr < p.R;  // K % 16 == 0 and R % 8 == 0
   };
   uint32_t tile = blockIdx.x;
   if (tile < p.ntiles) {
     locate(tile);
-    load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+    load_patch<ESZ, CPL>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
   }
   float ts = 0.0f;
   if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
   // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
   constexpr bool QUARTER = RHT && MODE == kSR && ESZ == 2;
+  uint32_t sflip[16];  // the transform's sign of token t: 0 or 2^31
+#pragma unroll
+  for (int t = 0; t < 16; ++t) sflip[t] = RHT ? ((p.sign_word >> t) & 1u) << 31 : 0u;
   __shared__ SrTables tab;
   float yts = 0.0f;
   bool recip_ok = false;
@@ -799,18 +870,18 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   for (; tile < p.ntiles; tile += gridDim.x) {
     if constexpr (PASS1) {
       // the next tile's loads go out before this tile's maxima
-      Raw8<ESZ> vn[16];
+      RawN<ESZ, CPL> vn[16];
       const bool more = tile + gridDim.x < p.ntiles;
       if (more) {
         locate(tile + gridDim.x);
-        load_patch<ESZ>(vn, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+        load_patch<ESZ, CPL>(vn, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < CPL; ++c) {
         float u[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) u[t] = raw8_elem<ESZ>(v[t], c);
-        if constexpr (RHT) rht16<false>(u, p.sign_word);
+        for (int t = 0; t < 16; ++t) u[t] = rawn_elem_signed<ESZ, CPL>(v[t], c, sflip[t]);
+        rht16_butterfly<false>(u);
         mx = max(mx, __float_as_uint(block_absmax(u)));
       }
       if (more) {
@@ -826,7 +897,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
 #pragma unroll
       for (int t = 0; t < 16; ++t)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) ab = fmaxf(ab, fabsf(raw8_elem<ESZ>(v[t], c)));
+        for (int c = 0; c < 8; ++c) ab = fmaxf(ab, fabsf(rawn_elem<ESZ, CPL>(v[t], c)));
       ab = fmaxf(ab, __shfl_xor(ab, 1, 64));
       sb2d = block_scale(ab, 6.0f, ts, S2d);
       e2d = encode_factor(S2d, ts);
@@ -847,19 +918,30 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       if (valid && (tj & 1u) == 0) p.scales[(rr / 16) * KB + kk / 16] = static_cast<uint8_t>(sb2d);
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < CPL; ++c) {
       float u[16];
+      if constexpr (RHT) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) u[t] = raw8_elem<ESZ>(v[t], c);
-      if constexpr (RHT) rht16<!QUARTER>(u, p.sign_word);
+        for (int t = 0; t < 16; ++t) u[t] = rawn_elem_signed<ESZ, CPL>(v[t], c, sflip[t]);
+        rht16_butterfly<!QUARTER>(u);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) u[t] = rawn_elem<ESZ, CPL>(v[t], c);
+      }
       const uint64_t i0 = static_cast<uint64_t>(rr + c) * static_cast<uint64_t>(p.K) + static_cast<uint64_t>(kk);
       if constexpr (RHT) {
         if (p.rht_out && valid) {
-          const float f = QUARTER ? 0.25f : 1.0f;
           float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
+          float w[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            o[q] = make_float4(u[4 * q] * f, u[4 * q + 1] * f, u[4 * q + 2] * f, u[4 * q + 3] * f);
+          for (int t = 0; t < 16; ++t) {
+            // opaque copy: the quarters stay in this branch (not hoisted as common with the encode's)
+            w[t] = u[t];
+            asm volatile("" : "+v"(w[t]));
+            if constexpr (QUARTER) w[t] = w[t] * 0.25f;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
         }
       }
       uint32_t sb, w0, w1;
@@ -872,8 +954,8 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
         encode_block<MODE>(u, block_absmax(u), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       }
       // LDS row rho = Y-row within the tile; 8-byte chunk ti stored at position ti ^ tj (= ti ^
-      // (rho >> 3)) so that the 16 column groups of a wave hit distinct banks.
-      const uint32_t rho = 8 * tj + c;
+      // (rho / CPL)) so that the 16 column groups of a wave hit distinct banks.
+      const uint32_t rho = CPL * tj + c;
       *reinterpret_cast<uint2 *>(lds_codes + rho * (kColTokens / 2) + 8 * (ti ^ tj)) = make_uint2(w0, w1);
       lds_scales[rho * (kColTokens / 16) + ti] = static_cast<uint8_t>(sb);
     }
@@ -881,15 +963,15 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     // the next tile's loads go out before this tile's output leaves LDS
     if (tile + gridDim.x < p.ntiles) {
       locate(tile + gridDim.x);
-      load_patch<ESZ>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
+      load_patch<ESZ, CPL>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
     }
     __syncthreads();
-    // codes: 128 rows x 128 B; 8 lanes per row, 16 B each
+    // codes: COLS rows x 128 B; 8 lanes per row, 16 B each
 #pragma unroll
-    for (int it = 0; it < (kColCols * kColTokens / 2) / (16 * kThreads); ++it) {
+    for (int it = 0; it < (COLS * kColTokens / 2) / (16 * kThreads); ++it) {
       const uint32_t idx = threadIdx.x + kThreads * it;
       const uint32_t rho = idx >> 3, s = idx & 7u;
-      const uint32_t sw = (rho >> 3) & 15u;
+      const uint32_t sw = (rho / CPL) & 15u;
       const uint32_t p0 = (2 * s) ^ sw;
       uint4 val = *reinterpret_cast<const uint4 *>(lds_codes + rho * (kColTokens / 2) + 8 * (p0 & ~1u));
       if (p0 & 1u) val = make_uint4(val.z, val.w, val.x, val.y);
@@ -906,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       }
     }
     if constexpr (!B2D) {
-      if (threadIdx.x < kColCols) {
+      if (threadIdx.x < COLS) {
         const uint32_t rho = threadIdx.x;
         const int64_t row = tR0 + rho;
         if (row < p.R) {
@@ -977,18 +1059,20 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
 
   // geometry of the pass-2 kernels (needed for the transform variants of pass 1 as well)
   RowArgs ra{};
-  ColArgs ca{};
-  uint32_t col_tiles = 0;
+  ColArgs ca8{}, ca4{};  // column-wise tiles of 256 tokens x 128 / 64 columns (8 / 4 per lane)
   if (!colwise) {
     ra = RowArgs{x, ldx_bytes, static_cast<uint32_t>(a.R * (a.K / 16)), make_fastdiv(static_cast<uint32_t>(a.K / 16)), a.K,
                  a.workspace, 0, a.workspace, a.data, a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out,
                  ts_div, gs};
   } else {
-    const uint32_t ntr = static_cast<uint32_t>((a.R + kColCols - 1) / kColCols);
     const uint32_t ntk = static_cast<uint32_t>((a.K + kColTokens - 1) / kColTokens);
-    col_tiles = ntr * ntk;
-    ca = ColArgs{x, ldx_bytes, a.K, a.R, col_tiles, make_fastdiv(ntr), a.workspace, 0, a.workspace, a.data,
-                 a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out, ts_div, gs};
+    auto col_args = [&](int64_t cols) {
+      const uint32_t ntr = static_cast<uint32_t>((a.R + cols - 1) / cols);
+      return ColArgs{x, ldx_bytes, a.K, a.R, ntr * ntk, make_fastdiv(ntr), a.workspace, 0, a.workspace, a.data,
+                     a.scales, a.ts, key0, key1, a.stream_id, a.sign_word, a.rht_out, ts_div, gs};
+    };
+    ca8 = col_args(128);
+    ca4 = col_args(64);
   }
 
   // ---- pass 1
@@ -1006,10 +1090,11 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   } else {
     // one round of resident workgroups: a second, partial round would run at a fraction of the
     // machine's bandwidth
-    const void *k1 = reinterpret_cast<const void *>(&col_kernel<ESZ, kRNE, true, false, true, false>);
+    const void *k1 = reinterpret_cast<const void *>(&col_kernel<ESZ, kRNE, true, false, true, false, 4>);
     const uint32_t res = resident_groups(k1);
-    nparts = clamp_grid(col_tiles, res > 0 && res < kPass1Parts ? res : kPass1Parts);
-    hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false>), dim3(nparts, G), dim3(kThreads), 0, a.stream, ca);
+    nparts = clamp_grid(ca4.ntiles, res > 0 && res < kPass1Parts ? res : kPass1Parts);
+    hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false, 4>), dim3(nparts, G), dim3(kThreads), 0, a.stream,
+                       ca4);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1050,15 +1135,21 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     else
       hipLaunchKernelGGL((row2d_kernel<ESZ, false>), dim3(grid, G), dim3(kThreads), 0, a.stream, r2);
   } else {
-    ca.nparts = nparts;
+    ca8.nparts = nparts;
+    ca4.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
-    const dim3 grid(clamp_grid(col_tiles, kPass2Grid), G), block(kThreads);
-#define NVFP4_COL(MODE_, RHT_, B2D_)                                                                        \
-  do {                                                                                                     \
-    if (aligned)                                                                                           \
-      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, true>), grid, block, 0, a.stream, ca); \
-    else                                                                                                   \
-      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, false>), grid, block, 0, a.stream, ca); \
+    const dim3 block(kThreads);
+    // stochastic rounding holds 4 columns per lane (fewer registers, more waves per SIMD for its
+    // VALU-bound encode); the other modes 8
+#define NVFP4_COL(MODE_, RHT_, B2D_)                                                                          \
+  do {                                                                                                       \
+    constexpr int CPL_ = MODE_ == kSR ? 4 : 8;                                                               \
+    const ColArgs &cc = CPL_ == 4 ? ca4 : ca8;                                                               \
+    const dim3 grid(clamp_grid(cc.ntiles, kPass2Grid), G);                                                   \
+    if (aligned)                                                                                             \
+      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, true, CPL_>), grid, block, 0, a.stream, cc); \
+    else                                                                                                     \
+      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, false, CPL_>), grid, block, 0, a.stream, cc); \
   } while (0)
     if (b2d && fos)
       NVFP4_COL(kFourOverSix, false, true);
