@@ -173,11 +173,18 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // (measured), but the compiler's builtin for it does not tie its first operand to the destination,
 // so bytes accumulated through the builtin are lost; the instruction is therefore issued here with
 // the accumulated word as a tied operand.
-template <int SEL>
+// FIRST: the accumulator's first conversion (byte 0).  The four conversions into one accumulator
+// write all four bytes, so the first needs no initial value: its operand is output-only.
+template <int SEL, bool FIRST = false>
 __device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t acc, float x, uint32_t seed) {
   const f32x2 src = {x, 0.0f};
   const float scale = 8388608.0f;  // 2^23: the instruction converts x / 2^23
-  if constexpr (SEL == 0)
+  if constexpr (FIRST) {
+    static_assert(SEL == 0, "the first conversion writes byte 0");
+    uint32_t out;
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "=v"(out) : "v"(src), "v"(seed), "v"(scale));
+    return out;
+  } else if constexpr (SEL == 0)
     asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(src), "v"(seed), "v"(scale));
   else if constexpr (SEL == 1)
     asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(src), "v"(seed), "v"(scale));
@@ -192,13 +199,13 @@ template <int T>  // element T of 8; nw = ~(its Philox word)
 __device__ __forceinline__ void sr_elem(float y, float e, uint32_t nw, uint32_t &even, uint32_t &odd) {
   const float xs = __builtin_copysignf(__builtin_ceilf((fabsf(y) * e) * 8388608.0f), y);
   if constexpr ((T & 1) != 0)  // r16 = high half of the word
-    odd = cvt_sr_byte<(T >> 1)>(odd, xs, nw | 0xFFFFu);
+    odd = cvt_sr_byte<(T >> 1), T == 1>(odd, xs, nw | 0xFFFFu);
   else  // r16 = low half of the word
-    even = cvt_sr_byte<(T >> 1)>(even, xs, (nw << 16) | 0xFFFFu);
+    even = cvt_sr_byte<(T >> 1), T == 0>(even, xs, (nw << 16) | 0xFFFFu);
 }
 
 __device__ __forceinline__ uint32_t pack8_sr(const float *y, float e, const u32x4 &w) {
-  uint32_t even = 0u, odd = 0u;  // codes of even / odd elements in the low nibble of byte T >> 1
+  uint32_t even, odd;  // codes of even / odd elements in the low nibble of byte T >> 1
   const uint32_t n0 = ~w.x, n1 = ~w.y, n2 = ~w.z, n3 = ~w.w;
   sr_elem<0>(y[0], e, n0, even, odd);
   sr_elem<1>(y[1], e, n0, even, odd);
@@ -227,13 +234,13 @@ template <int T>  // element T of 8; w = its Philox word
 __device__ __forceinline__ void sr_elem_folded(float y, float E, uint32_t w, uint32_t &even, uint32_t &odd) {
   const float xs = __builtin_copysignf(__builtin_ceilf(fabsf(y) * E), y);
   if constexpr ((T & 1) != 0)
-    odd = cvt_sr_byte<(T >> 1)>(odd, xs, ~w | 0xFFFFu);
+    odd = cvt_sr_byte<(T >> 1), T == 1>(odd, xs, ~w | 0xFFFFu);
   else
-    even = cvt_sr_byte<(T >> 1)>(even, xs, seed_low_half(w));
+    even = cvt_sr_byte<(T >> 1), T == 0>(even, xs, seed_low_half(w));
 }
 
 __device__ __forceinline__ uint32_t pack8_sr_folded(const float *y, float E, const u32x4 &w) {
-  uint32_t even = 0u, odd = 0u;
+  uint32_t even, odd;
   sr_elem_folded<0>(y[0], E, w.x, even, odd);
   sr_elem_folded<1>(y[1], E, w.x, even, odd);
   sr_elem_folded<2>(y[2], E, w.y, even, odd);
@@ -917,8 +924,9 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       }
       if (valid && (tj & 1u) == 0) p.scales[(rr / 16) * KB + kk / 16] = static_cast<uint8_t>(sb2d);
     }
+    uint64_t i0 = static_cast<uint64_t>(rr) * static_cast<uint64_t>(p.K) + static_cast<uint64_t>(kk);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
+    for (int c = 0; c < CPL; ++c, i0 += static_cast<uint64_t>(p.K)) {  // i0: logical index of (rr + c, kk)
       float u[16];
       if constexpr (RHT) {
 #pragma unroll
@@ -928,7 +936,6 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) u[t] = rawn_elem<ESZ, CPL>(v[t], c);
       }
-      const uint64_t i0 = static_cast<uint64_t>(rr + c) * static_cast<uint64_t>(p.K) + static_cast<uint64_t>(kk);
       if constexpr (RHT) {
         if (p.rht_out && valid) {
           float4 *o = reinterpret_cast<float4 *>(p.rht_out + i0);
