@@ -3,7 +3,7 @@
 // Two passes per tensor, both on the caller's stream:
 //   pass 1  tensor amax: every workgroup writes the largest |y| it saw to workspace[blockIdx.x]
 //           (plain tensors: amax_kernel; with the Hadamard transform the maximum is taken over the
-//           transformed values, by the pass-2 kernels compiled with PASS1 = true);
+//           transformed values: row1d_kernel compiled with PASS1 = true, col_amax_kernel);
 //   pass 2  every workgroup reduces the partial maxima itself (no atomics, no zeroed memory),
 //           derives ts = amax / 2688, and encodes its blocks: block amax -> E4M3 scale -> E2M1
 //           codes (nearest-even, stochastic or Four-over-Six) -> packed nibbles.
@@ -17,12 +17,13 @@
 // except NaN (checked exhaustively), so v = y * e is fed to it directly.
 //
 // Layouts:
-//   row1d_kernel   ROW mode, 1D blocks: one lane per 16-element block (32 B of bf16 in, 8 B out).
-//   row2d_kernel   ROW mode, 16x16 tiles: a lane holds 16 rows x 8 columns; a lane pair is a tile.
-//   col_kernel     COLWISE: a lane holds 16 tokens x 8 columns, i.e. one block of each of 8 rows of
-//                  x^T; a 256-lane workgroup covers 256 tokens x 128 columns and transposes its
-//                  packed output through LDS so that every row segment leaves as 128 contiguous
-//                  bytes.
+//   row1d_kernel    ROW mode, 1D blocks: one lane per 16-element block (32 B of bf16 in, 8 B out).
+//   row2d_kernel    ROW mode, 16x16 tiles: a lane holds 16 rows x 8 columns; a lane pair is a tile.
+//   col_kernel      COLWISE: a lane holds 16 tokens x CPL columns (8, or 4 for stochastic
+//                   rounding), i.e. one block of each of CPL rows of x^T; a 256-lane workgroup
+//                   covers 256 tokens x 16 CPL columns and transposes its packed output through LDS
+//                   so that every row segment leaves as 128 contiguous bytes.
+//   col_amax_kernel COLWISE pass 1 with the transform: a wave reads 16 rows x 1 KiB strips.
 #include <type_traits>
 
 #include "nvfp4_device.hpp"
@@ -830,19 +831,17 @@ struct ColArgs {
 
 constexpr int kColTokens = 256;  // per workgroup tile
 
-template <int ESZ, int MODE, bool RHT, bool B2D, bool PASS1, bool ALIGNED, int CPL>
+template <int ESZ, int MODE, bool RHT, bool B2D, bool ALIGNED, int CPL>
 __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   static_assert(CPL == 8 || (CPL == 4 && !B2D), "16x16 tiles take a lane pair of 8 columns each");
   constexpr int COLS = 16 * CPL;  // columns of x (rows of Y) per workgroup tile
   enter_group(p, p.nparts);
-  p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   p.stream_id += blockIdx.y;
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS * (kColTokens / 2)];
   __shared__ __attribute__((aligned(16))) uint8_t lds_scales[COLS * (kColTokens / 16)];
   const uint32_t ti = threadIdx.x >> 4;  // token group (16 tokens)
   const uint32_t tj = threadIdx.x & 15;  // column group (CPL columns)
   const int64_t KB = p.K / 16;
-  uint32_t mx = 0;
   RawN<ESZ, CPL> v[16];
   int64_t K0 = 0, R0 = 0, kk = 0, rr = 0;
   bool valid = false;
@@ -859,8 +858,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     locate(tile);
     load_patch<ESZ, CPL>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
   }
-  float ts = 0.0f;
-  if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
+  const float ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
   // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
   constexpr bool QUARTER = RHT && MODE == kSR && ESZ == 2;
   uint32_t sflip[16];  // the transform's sign of token t: 0 or 2^31
@@ -869,34 +867,12 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   __shared__ SrTables tab;
   float yts = 0.0f;
   bool recip_ok = false;
-  if constexpr (MODE == kSR && !PASS1) {
+  if constexpr (MODE == kSR) {
     build_sr_tables<ESZ, QUARTER>(tab, ts);
     recip_ok = ts >= 0x1p-100f && ts <= 0x1p100f;
     yts = 1.0f / ts;
   }
   for (; tile < p.ntiles; tile += gridDim.x) {
-    if constexpr (PASS1) {
-      // the next tile's loads go out before this tile's maxima
-      RawN<ESZ, CPL> vn[16];
-      const bool more = tile + gridDim.x < p.ntiles;
-      if (more) {
-        locate(tile + gridDim.x);
-        load_patch<ESZ, CPL>(vn, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
-      }
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float u[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) u[t] = rawn_elem_signed<ESZ, CPL>(v[t], c, sflip[t]);
-        rht16_butterfly<false>(u);
-        mx = max(mx, __float_as_uint(block_absmax(u)));
-      }
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) v[t] = vn[t];
-      }
-      continue;
-    }
     float S2d = 0.0f, e2d = 0.0f;
     uint32_t sb2d = 0;
     if constexpr (B2D) {
@@ -1012,7 +988,41 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     }
     __syncthreads();
   }
-  if constexpr (PASS1) write_partial(RHT ? quarter_bits(mx) : mx, p.partial_out);
+}
+
+// Pass 1 of the column-wise Hadamard variants: the largest |H16 D u| / 4 over every 16-token block
+// of every column, the values col_kernel's transform produces (the 1/4 taken once, quarter_bits).
+// The order of the blocks does not matter for a maximum, so each wave takes strips of 16 tokens x
+// (64 lanes x 16 bytes): lane l holds 16 bytes (8 bf16 / 4 f32 columns) of each of the strip's 16
+// rows, and a row is read as 1 KiB contiguous per wave (col_kernel's lane layout reads 128-256 B
+// pieces).  Consecutive strips of a token group go to consecutive waves.
+template <int ESZ>
+__global__ __launch_bounds__(kThreads) void col_amax_kernel(ColArgs p, FastDiv ns, uint32_t nunits) {  // ns: strips per group
+  constexpr int CPL = 16 / ESZ;  // columns per lane
+  enter_group(p, p.nparts);
+  p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  uint32_t sflip[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) sflip[t] = ((p.sign_word >> t) & 1u) << 31;
+  uint32_t mx = 0;
+  for (uint32_t u = (blockIdx.x * kThreads + threadIdx.x) >> 6; u < nunits; u += nwaves) {
+    const uint32_t g = fdiv(u, ns);
+    const int64_t kk = 16 * static_cast<int64_t>(g);
+    const int64_t rr = (static_cast<int64_t>(u - g * ns.d) * 64 + lane) * CPL;
+    RawN<ESZ, CPL> v[16];
+    load_patch<ESZ, CPL>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, rr < p.R);  // R % 8 == 0
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float y[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) y[t] = rawn_elem_signed<ESZ, CPL>(v[t], c, sflip[t]);
+      rht16_butterfly<false>(y);
+      mx = max(mx, __float_as_uint(block_absmax(y)));
+    }
+  }
+  write_partial(quarter_bits(mx), p.partial_out);
 }
 
 __global__ void zero_ts_kernel(float *ts, uint32_t n) {
@@ -1097,11 +1107,11 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   } else {
     // one round of resident workgroups: a second, partial round would run at a fraction of the
     // machine's bandwidth
-    const void *k1 = reinterpret_cast<const void *>(&col_kernel<ESZ, kRNE, true, false, true, false, 4>);
-    const uint32_t res = resident_groups(k1);
-    nparts = clamp_grid(ca4.ntiles, res > 0 && res < kPass1Parts ? res : kPass1Parts);
-    hipLaunchKernelGGL((col_kernel<ESZ, kRNE, true, false, true, false, 4>), dim3(nparts, G), dim3(kThreads), 0, a.stream,
-                       ca4);
+    const uint32_t nstrips = static_cast<uint32_t>((a.R + 64 * (16 / ESZ) - 1) / (64 * (16 / ESZ)));
+    const uint32_t nunits = static_cast<uint32_t>(a.K / 16) * nstrips;
+    const uint32_t res = resident_groups(reinterpret_cast<const void *>(&col_amax_kernel<ESZ>));
+    nparts = clamp_grid((nunits + 3) / 4, res > 0 && res < kPass1Parts ? res : kPass1Parts);
+    hipLaunchKernelGGL(col_amax_kernel<ESZ>, dim3(nparts, G), dim3(kThreads), 0, a.stream, ca4, make_fastdiv(nstrips), nunits);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1154,9 +1164,9 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const ColArgs &cc = CPL_ == 4 ? ca4 : ca8;                                                               \
     const dim3 grid(clamp_grid(cc.ntiles, kPass2Grid), G);                                                   \
     if (aligned)                                                                                             \
-      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, true, CPL_>), grid, block, 0, a.stream, cc); \
+      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, true, CPL_>), grid, block, 0, a.stream, cc); \
     else                                                                                                     \
-      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, false, CPL_>), grid, block, 0, a.stream, cc); \
+      hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, false, CPL_>), grid, block, 0, a.stream, cc); \
   } while (0)
     if (b2d && fos)
       NVFP4_COL(kFourOverSix, false, true);
