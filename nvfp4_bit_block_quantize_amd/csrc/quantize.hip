@@ -73,6 +73,29 @@ __device__ __forceinline__ void unpack16(const Raw16<ESZ> &r, float (&y)[16]) {
   }
 }
 
+// rht16 (nvfp4_device.hpp) in two parts: the random signs D are applied while unpacking
+// (unpack16_signed, rawn_elem_signed), then the butterfly below, with the 1/4 left to the caller
+// when SCALE is false.  Same operations in the same order as rht16.
+template <bool SCALE = true>
+__device__ __forceinline__ void rht16_butterfly(float (&u)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * h) {
+#pragma unroll
+      for (int m = i; m < i + h; ++m) {
+        float a = u[m], b = u[m + h];
+        u[m] = a + b;
+        u[m + h] = a - b;
+      }
+    }
+  }
+  if constexpr (SCALE) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) u[t] = u[t] * 0.25f;
+  }
+}
+
 // unpack16 with the Hadamard transform's random signs applied (bit t of sign_word flips element t);
 // the low bf16 half takes its flip as an addition of 2^31 (see rawn_elem_signed).
 template <int ESZ>
@@ -665,6 +688,19 @@ struct Row2dArgs {
   GroupStrides g;
 };
 
+// An empty asm that claims to modify the patch's registers: values unpacked from it before are not
+// reused after, the compiler unpacks again (one instruction per element) instead of holding them.
+template <int ESZ, int N>
+__device__ __forceinline__ void opaque_patch(RawN<ESZ, N> (&v)[16]) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int i = 0; i < (N * ESZ >= 16 ? N * ESZ / 16 : 1); ++i) {
+      asm volatile("" : "+v"(v[t].v[i].x), "+v"(v[t].v[i].y));
+      if constexpr (N * ESZ >= 16) asm volatile("" : "+v"(v[t].v[i].z), "+v"(v[t].v[i].w));
+    }
+}
+
 template <int ESZ, int N = 8>
 __device__ __forceinline__ void load_patch(RawN<ESZ, N> (&v)[16], const uint8_t *__restrict__ base, int64_t ld_bytes,
                                            bool valid) {
@@ -770,6 +806,8 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) ab = fmaxf(ab, fabsf(raw8_elem<ESZ>(v[t], c)));
     ab = fmaxf(ab, __shfl_xor(ab, 1, 64));
+    // unpack again below rather than keep all 128 values unpacked (which costs 128 registers)
+    opaque_patch<ESZ, 8>(v);
     float S;
     uint32_t sb = block_scale(ab, 6.0f, ts, S);
     float e = encode_factor(S, ts);
@@ -777,10 +815,12 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
       // Four-over-Six on the tile: target 4 only if its tile error is strictly lower
       const bool even = (lane & 1u) == 0;
       const float sse6 = tile_sse_rows<ESZ>(v, e, S, ts, even);
+      opaque_patch<ESZ, 8>(v);
       float S4;
       const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
       const float e4 = encode_factor(S4, ts);
       const float sse4 = tile_sse_rows<ESZ>(v, e4, S4, ts, even);
+      opaque_patch<ESZ, 8>(v);
       if (sse4 < sse6) {
         sb = sb4;
         e = e4;
@@ -882,16 +922,19 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) ab = fmaxf(ab, fabsf(rawn_elem<ESZ, CPL>(v[t], c)));
       ab = fmaxf(ab, __shfl_xor(ab, 1, 64));
+      opaque_patch<ESZ, CPL>(v);  // unpack again below rather than hold 128 values
       sb2d = block_scale(ab, 6.0f, ts, S2d);
       e2d = encode_factor(S2d, ts);
       if constexpr (MODE == kFourOverSix) {
         // Four-over-Six on the tile: this lane holds 8 rows (top or bottom half) of the tile
         const bool even = (tj & 1u) == 0;
         const float sse6 = tile_sse_cols<ESZ>(v, e2d, S2d, ts, even);
+        opaque_patch<ESZ, CPL>(v);
         float S4;
         const uint32_t sb4 = block_scale(ab, 4.0f, ts, S4);
         const float e4 = encode_factor(S4, ts);
         const float sse4 = tile_sse_cols<ESZ>(v, e4, S4, ts, even);
+        opaque_patch<ESZ, CPL>(v);
         if (sse4 < sse6) {
           sb2d = sb4;
           S2d = S4;
@@ -1156,13 +1199,21 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     ca4.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
     const dim3 block(kThreads);
-    // stochastic rounding holds 4 columns per lane (fewer registers, more waves per SIMD for its
-    // VALU-bound encode); the other modes 8
+    // Stochastic rounding and 1D nearest-even hold 4 columns per lane (fewer registers: more waves
+    // per SIMD, twice the tiles); 16x16 tiles and the error-comparing modes 8.  Nearest-even runs one
+    // round of resident workgroups (a few tiles each, the next one loading during the current one);
+    // stochastic rounding, VALU-bound, two rounds of workgroups.
 #define NVFP4_COL(MODE_, RHT_, B2D_)                                                                          \
   do {                                                                                                       \
-    constexpr int CPL_ = MODE_ == kSR ? 4 : 8;                                                               \
+    constexpr int CPL_ = (MODE_ == kSR || (MODE_ == kRNE && !B2D_)) ? 4 : 8;                                 \
     const ColArgs &cc = CPL_ == 4 ? ca4 : ca8;                                                               \
-    const dim3 grid(clamp_grid(cc.ntiles, kPass2Grid), G);                                                   \
+    uint32_t cap_ = kPass2Grid;                                                                              \
+    if (MODE_ == kRNE && CPL_ == 4) {                                                                        \
+      const uint32_t res_ = resident_groups(                                                                 \
+          reinterpret_cast<const void *>(&col_kernel<ESZ, MODE_, RHT_, B2D_, true, CPL_>));                  \
+      if (res_ > 0 && res_ < cap_) cap_ = res_;                                                              \
+    }                                                                                                        \
+    const dim3 grid(clamp_grid(cc.ntiles, cap_), G);                                                         \
     if (aligned)                                                                                             \
       hipLaunchKernelGGL((col_kernel<ESZ, MODE_, RHT_, B2D_, true, CPL_>), grid, block, 0, a.stream, cc); \
     else                                                                                                     \
