@@ -362,24 +362,35 @@ __device__ __forceinline__ uint32_t block_scale_byte(float ab, float ts, float y
 }
 
 // Per-workgroup tables of the 127 scale bytes a block can get (s <= 448 rounds to at most 0x7E):
-// e[b] = encode_factor(S(b), ts), and E[b] = e[b] * FOLD where the folded stochastic rounding
-// applies to that factor (encode_block_sr), else -1.
-struct SrTables {
+// e[b] = encode_factor(S(b), ts), and E[b] = the factor the shortcut encode multiplies by where it
+// applies to that factor, else -1:
+//   stochastic rounding: e * 2^23 (e * 2^21 with the quarter folded), encode_block_sr;
+//   nearest-even: e, or e / 4 with the Hadamard quarter folded (bf16), encode_block_rne_tab.
+struct FactorTables {
   float e[128];
   float E[128];
 };
 
-template <int ESZ, bool QUARTER>
-__device__ __forceinline__ void build_sr_tables(SrTables &t, float ts) {
+template <int MODE, int ESZ, bool QUARTER>
+__device__ __forceinline__ void build_factor_tables(FactorTables &t, float ts) {
   if (threadIdx.x < 128) {
     const uint32_t b = threadIdx.x;
     const float S = b < 8 ? static_cast<float>(b) * 0.001953125f
                           : __uint_as_float((((b >> 3) + 120u) << 23) | ((b & 7u) << 20));
     const float e = encode_factor(S, ts);
-    constexpr float kMinFactor = ESZ == 2 ? 0x1p-14f : 1.0f;
-    const bool fold = e == 0.0f || (e >= kMinFactor && e <= 0x1p100f);
+    bool fold;
+    float E;
+    if constexpr (MODE == kSR) {
+      constexpr float kMinFactor = ESZ == 2 ? 0x1p-14f : 1.0f;
+      fold = e == 0.0f || (e >= kMinFactor && e <= 0x1p100f);
+      E = e * (QUARTER ? 0x1p21f : 0x1p23f);
+    } else {
+      // e / 4 is exact from 2^-124 up; RN(y e) of y = u / 4 (exact for bf16) is then RN(u (e / 4))
+      fold = e == 0.0f || (e < __builtin_inff() && (!QUARTER || e >= 0x1p-124f));
+      E = QUARTER ? e * 0.25f : e;
+    }
     t.e[b] = e;
-    t.E[b] = fold ? e * (QUARTER ? 0x1p21f : 0x1p23f) : -1.0f;
+    t.E[b] = fold ? E : -1.0f;
   }
   __syncthreads();
 }
@@ -398,10 +409,10 @@ __device__ __forceinline__ void build_sr_tables(SrTables &t, float ts) {
 //   - for e = 0 (a zero block scale): both are 0 (y' finite) or the same NaN;
 //   - and E = e 2^23 stays finite for e <= 2^100.
 // Other factors (inf: S * ts underflowed; NaN) take the unfolded path.  The factor of each scale
-// byte, and whether it folds, come from the workgroup's tables (build_sr_tables).
+// byte, and whether it folds, come from the workgroup's tables (build_factor_tables).
 template <int ESZ, bool QUARTER>
 __device__ __forceinline__ void encode_block_sr(float (&y)[16], float ts, float yts, bool recip_ok,
-                                                const SrTables &tab, uint64_t i0, uint32_t key0, uint32_t key1,
+                                                const FactorTables &tab, uint64_t i0, uint32_t key0, uint32_t key1,
                                                 uint32_t stream_id, uint32_t &sbyte, uint32_t &w0, uint32_t &w1) {
   static_assert(ESZ == 2 || !QUARTER, "the quarter of an fp32 transform may round");
   float ab = block_absmax(y);
@@ -433,6 +444,41 @@ __device__ __forceinline__ void encode_block_sr(float (&y)[16], float ts, float 
     } else {
       w0 = pack8_sr(y, e, r0);
       w1 = pack8_sr(y + 8, e, r1);
+    }
+  }
+}
+
+// Nearest-even encode of one 1D block of y' = y (QUARTER: y' = y / 4), as encode_block<kRNE> of y':
+// scale byte through reciprocals (block_scale_byte), factor from the tables, codes of RN(y E).
+template <int ESZ, bool QUARTER>
+__device__ __forceinline__ void encode_block_rne_tab(float (&y)[16], float ts, float yts, bool recip_ok,
+                                                     const FactorTables &tab, uint32_t &sbyte, uint32_t &w0,
+                                                     uint32_t &w1) {
+  static_assert(ESZ == 2 || !QUARTER, "the quarter of an fp32 transform may round");
+  float ab = block_absmax(y);
+  if constexpr (QUARTER) ab = ab * 0.25f;  // = max RN(|y| / 4): rounding is monotone
+  sbyte = block_scale_byte(ab, ts, yts, recip_ok);
+  const float E = tab.E[sbyte];
+  if (E >= 0.0f) {
+    w0 = pack8_rne(y, E);
+    w1 = pack8_rne(y + 8, E);
+  } else {
+    const float e = tab.e[sbyte];
+    if constexpr (QUARTER) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) y[t] = y[t] * 0.25f;
+    }
+    if (__builtin_isinf(e)) {
+      w0 = 0u;
+      w1 = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        w0 |= code_degenerate(y[t]) << (4 * t);
+        w1 |= code_degenerate(y[8 + t]) << (4 * t);
+      }
+    } else {
+      w0 = pack8_rne(y, e);
+      w1 = pack8_rne(y + 8, e);
     }
   }
 }
@@ -606,13 +652,15 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   if (b < p.nblocks) cur = load_raw16<ESZ>(src(b));
   float ts = 0.0f;
   if constexpr (!PASS1) ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
-  // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
-  constexpr bool QUARTER = RHT && (PASS1 || (MODE == kSR && ESZ == 2));
-  __shared__ SrTables tab;
+  // stochastic rounding and 1D nearest-even of bf16 keep the transform's 1/4 out of the elements
+  // (encode_block_sr, encode_block_rne_tab)
+  constexpr bool QUARTER = RHT && (PASS1 || ((MODE == kSR || MODE == kRNE) && ESZ == 2));
+  constexpr bool TABLES = !PASS1 && (MODE == kSR || MODE == kRNE);
+  __shared__ FactorTables tab;
   float yts = 0.0f;
   bool recip_ok = false;
-  if constexpr (MODE == kSR && !PASS1) {
-    build_sr_tables<ESZ, QUARTER>(tab, ts);
+  if constexpr (TABLES) {
+    build_factor_tables<MODE, ESZ, QUARTER>(tab, ts);
     recip_ok = ts >= 0x1p-100f && ts <= 0x1p100f;
     yts = 1.0f / ts;
   }
@@ -650,6 +698,8 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
       uint32_t sb, w0, w1;
       if constexpr (MODE == kSR)
         encode_block_sr<ESZ, QUARTER>(y, ts, yts, recip_ok, tab, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+      else if constexpr (MODE == kRNE)
+        encode_block_rne_tab<ESZ, QUARTER>(y, ts, yts, recip_ok, tab, sb, w0, w1);
       else
         encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       *reinterpret_cast<uint2 *>(p.data + (i0 >> 1)) = make_uint2(w0, w1);
@@ -899,16 +949,18 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
     load_patch<ESZ, CPL>(v, p.x + kk * p.ldx_bytes + rr * ESZ, p.ldx_bytes, valid);
   }
   const float ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
-  // stochastic rounding of bf16 keeps the transform's 1/4 out of the elements (encode_block_sr)
-  constexpr bool QUARTER = RHT && MODE == kSR && ESZ == 2;
+  // stochastic rounding and 1D nearest-even of bf16 keep the transform's 1/4 out of the elements
+  // (encode_block_sr, encode_block_rne_tab)
+  constexpr bool QUARTER = RHT && (MODE == kSR || (MODE == kRNE && !B2D)) && ESZ == 2;
+  constexpr bool TABLES = MODE == kSR || (MODE == kRNE && !B2D);
   uint32_t sflip[16];  // the transform's sign of token t: 0 or 2^31
 #pragma unroll
   for (int t = 0; t < 16; ++t) sflip[t] = RHT ? ((p.sign_word >> t) & 1u) << 31 : 0u;
-  __shared__ SrTables tab;
+  __shared__ FactorTables tab;
   float yts = 0.0f;
   bool recip_ok = false;
-  if constexpr (MODE == kSR) {
-    build_sr_tables<ESZ, QUARTER>(tab, ts);
+  if constexpr (TABLES) {
+    build_factor_tables<MODE, ESZ, QUARTER>(tab, ts);
     recip_ok = ts >= 0x1p-100f && ts <= 0x1p100f;
     yts = 1.0f / ts;
   }
@@ -976,6 +1028,8 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
         sb = sb2d;
       } else if constexpr (MODE == kSR) {
         encode_block_sr<ESZ, QUARTER>(u, ts, yts, recip_ok, tab, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+      } else if constexpr (MODE == kRNE) {
+        encode_block_rne_tab<ESZ, QUARTER>(u, ts, yts, recip_ok, tab, sb, w0, w1);
       } else {
         encode_block<MODE>(u, block_absmax(u), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
       }
