@@ -345,27 +345,32 @@ __device__ __forceinline__ float div_by_recip(float a, float b, float y) {
 }
 
 constexpr float kRecip6 = 0x1.555556p-3f;  // RN(1 / 6)
+// RN(1 / T) for the search targets 5.5, 5, 4.5, 4
+constexpr float kRecipTargets[5] = {0x1.555556p-3f, 0x1.745d18p-3f, 0x1.99999ap-3f, 0x1.c71c72p-3f, 0x1p-2f};
 
 // Scale byte of a block with maximum ab (target 6), as block_scale computes it.  With ts in
 // [2^-100, 2^100] (recip_ok; yts = RN(1 / ts)) and ab = 0 or in [2^-90, 2^100], both divisions go
 // through div_by_recip: RN(ab / 6) is then normal, and RN(q / ts) is correctly rounded wherever it
 // is normal; where it is not (below 2^-126) both forms are far below 2^-10, the smallest value
 // that rounds to a nonzero scale, so the byte is 0 either way.
-__device__ __forceinline__ uint32_t block_scale_byte(float ab, float ts, float yts, bool recip_ok) {
+// Target T (yT = RN(1 / T)) for the Four-over-Six and search candidates: the same with ab / T.
+__device__ __forceinline__ uint32_t block_scale_byte(float ab, float ts, float yts, bool recip_ok, float T = 6.0f,
+                                                     float yT = kRecip6) {
   float S;
   if (recip_ok && (ab == 0.0f || (ab >= 0x1p-90f && ab <= 0x1p100f))) {
-    const float q = div_by_recip(ab, 6.0f, kRecip6);
+    const float q = div_by_recip(ab, T, yT);
     const float sc = fminf(div_by_recip(q, ts, yts), 448.0f);
     return e4m3_rne(sc, S);
   }
-  return block_scale(ab, 6.0f, ts, S);
+  return block_scale(ab, T, ts, S);
 }
 
 // Per-workgroup tables of the 127 scale bytes a block can get (s <= 448 rounds to at most 0x7E):
 // e[b] = encode_factor(S(b), ts), and E[b] = the factor the shortcut encode multiplies by where it
 // applies to that factor, else -1:
 //   stochastic rounding: e * 2^23 (e * 2^21 with the quarter folded), encode_block_sr;
-//   nearest-even: e, or e / 4 with the Hadamard quarter folded (bf16), encode_block_rne_tab.
+//   nearest-even: e, or e / 4 with the Hadamard quarter folded (bf16), encode_block_rne_tab;
+//   Four-over-Six and the scale search: the decoded scale S(b) (encode_block_tab).
 struct FactorTables {
   float e[128];
   float E[128];
@@ -384,6 +389,9 @@ __device__ __forceinline__ void build_factor_tables(FactorTables &t, float ts) {
       constexpr float kMinFactor = ESZ == 2 ? 0x1p-14f : 1.0f;
       fold = e == 0.0f || (e >= kMinFactor && e <= 0x1p100f);
       E = e * (QUARTER ? 0x1p21f : 0x1p23f);
+    } else if constexpr (MODE == kFourOverSix || MODE == kSearch) {
+      fold = true;  // E holds the decoded scale S(b) itself
+      E = S;
     } else {
       // e / 4 is exact from 2^-124 up; RN(y e) of y = u / 4 (exact for bf16) is then RN(u (e / 4))
       fold = e == 0.0f || (e < __builtin_inff() && (!QUARTER || e >= 0x1p-124f));
@@ -510,6 +518,36 @@ __device__ __forceinline__ void encode_block(const float (&y)[16], float ab, flo
         w0 = v0;
         w1 = v1;
       }
+    }
+  }
+}
+
+
+// encode_block<kFourOverSix / kSearch> with the candidates' scale bytes through reciprocals
+// (block_scale_byte) and their factors e and decoded scales S from the workgroup's tables: the same
+// candidates, codes and errors, so the same choice.
+template <int MODE>
+__device__ __forceinline__ void encode_block_tab(const float (&y)[16], float ts, float yts, bool recip_ok,
+                                                 const FactorTables &tab, uint32_t &sbyte, uint32_t &w0,
+                                                 uint32_t &w1) {
+  static_assert(MODE == kFourOverSix || MODE == kSearch, "candidate modes only");
+  const float ab = block_absmax(y);
+  sbyte = block_scale_byte(ab, ts, yts, recip_ok);
+  block_words<kRNE>(y, tab.e[sbyte], 0u, 0u, 0u, 0u, w0, w1);
+  constexpr int NT = MODE == kSearch ? 5 : 2;
+  float best = block_sse(y, w0, w1, tab.E[sbyte], ts);
+#pragma unroll
+  for (int ti = 1; ti < NT; ++ti) {
+    const int k = MODE == kSearch ? ti : 4;  // index of T in 6, 5.5, 5, 4.5, 4
+    const uint32_t sbx = block_scale_byte(ab, ts, yts, recip_ok, 6.0f - 0.5f * k, kRecipTargets[k]);
+    uint32_t v0, v1;
+    block_words<kRNE>(y, tab.e[sbx], 0u, 0u, 0u, 0u, v0, v1);
+    const float acc = block_sse(y, v0, v1, tab.E[sbx], ts);
+    if (acc < best) {
+      best = acc;
+      sbyte = sbx;
+      w0 = v0;
+      w1 = v1;
     }
   }
 }
@@ -655,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   // stochastic rounding and 1D nearest-even of bf16 keep the transform's 1/4 out of the elements
   // (encode_block_sr, encode_block_rne_tab)
   constexpr bool QUARTER = RHT && (PASS1 || ((MODE == kSR || MODE == kRNE) && ESZ == 2));
-  constexpr bool TABLES = !PASS1 && (MODE == kSR || MODE == kRNE);
+  constexpr bool TABLES = !PASS1;  // every 1D mode
   __shared__ FactorTables tab;
   float yts = 0.0f;
   bool recip_ok = false;
@@ -701,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
       else if constexpr (MODE == kRNE)
         encode_block_rne_tab<ESZ, QUARTER>(y, ts, yts, recip_ok, tab, sb, w0, w1);
       else
-        encode_block<MODE>(y, block_absmax(y), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+        encode_block_tab<MODE>(y, ts, yts, recip_ok, tab, sb, w0, w1);
       *reinterpret_cast<uint2 *>(p.data + (i0 >> 1)) = make_uint2(w0, w1);
       p.scales[i0 >> 4] = static_cast<uint8_t>(sb);
     }
@@ -952,7 +990,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
   // stochastic rounding and 1D nearest-even of bf16 keep the transform's 1/4 out of the elements
   // (encode_block_sr, encode_block_rne_tab)
   constexpr bool QUARTER = RHT && (MODE == kSR || (MODE == kRNE && !B2D)) && ESZ == 2;
-  constexpr bool TABLES = MODE == kSR || (MODE == kRNE && !B2D);
+  constexpr bool TABLES = !B2D;  // every 1D mode
   uint32_t sflip[16];  // the transform's sign of token t: 0 or 2^31
 #pragma unroll
   for (int t = 0; t < 16; ++t) sflip[t] = RHT ? ((p.sign_word >> t) & 1u) << 31 : 0u;
@@ -1031,7 +1069,7 @@ __global__ __launch_bounds__(kThreads) void col_kernel(ColArgs p) {
       } else if constexpr (MODE == kRNE) {
         encode_block_rne_tab<ESZ, QUARTER>(u, ts, yts, recip_ok, tab, sb, w0, w1);
       } else {
-        encode_block<MODE>(u, block_absmax(u), ts, i0, p.key0, p.key1, p.stream_id, sb, w0, w1);
+        encode_block_tab<MODE>(u, ts, yts, recip_ok, tab, sb, w0, w1);
       }
       // LDS row rho = Y-row within the tile; 8-byte chunk ti stored at position ti ^ tj (= ti ^
       // (rho / CPL)) so that the 16 column groups of a wave hit distinct banks.
@@ -1253,13 +1291,12 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     ca4.nparts = nparts;
     const bool aligned = (a.K % kColTokens) == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
     const dim3 block(kThreads);
-    // Stochastic rounding and 1D nearest-even hold 4 columns per lane (fewer registers: more waves
-    // per SIMD, twice the tiles); 16x16 tiles and the error-comparing modes 8.  Nearest-even runs one
-    // round of resident workgroups (a few tiles each, the next one loading during the current one);
-    // stochastic rounding, VALU-bound, two rounds of workgroups.
+    // 1D blocks hold 4 columns per lane (fewer registers: more waves per SIMD, twice the tiles);
+    // 16x16 tiles 8 (a lane pair is a tile).  Nearest-even runs one round of resident workgroups (a
+    // few tiles each, the next one loading during the current one); the VALU-bound modes two rounds.
 #define NVFP4_COL(MODE_, RHT_, B2D_)                                                                          \
   do {                                                                                                       \
-    constexpr int CPL_ = (MODE_ == kSR || (MODE_ == kRNE && !B2D_)) ? 4 : 8;                                 \
+    constexpr int CPL_ = B2D_ ? 8 : 4;                                                                       \
     const ColArgs &cc = CPL_ == 4 ? ca4 : ca8;                                                               \
     uint32_t cap_ = kPass2Grid;                                                                              \
     if (MODE_ == kRNE && CPL_ == 4) {                                                                        \

@@ -4,9 +4,10 @@
  *   1. b = 6 and every a in [2^lo, 2^hi) (argv 1, 2: exponents), stride argv 3;
  *   2. argv 4 random b in [2^-100, 2^100], 2 * 10^5 random a each, half of them next to b times a
  *      short number (quotients near short values and rounding midpoints);
- *   3. the scale byte: E4M3 rounding of min(RN(RN(ab / 6) / ts), 448) from the two corrected
- *      quotients against IEEE division, argv 5 random ts with 10^5 block maxima each, from 2^-40 to
- *      2^12 times the tensor maximum 2688 ts (quotients down into the subnormal range). */
+ *   3. the scale byte: E4M3 rounding of min(RN(RN(ab / T) / ts), 448) from the two corrected
+ *      quotients against IEEE division, for the targets T = 6, 5.5, 5, 4.5 and 4 in turn, argv 5
+ *      random ts with 10^5 block maxima each, from 2^-40 to 2^12 times the tensor maximum 2688 ts
+ *      (quotients down into the subnormal range). */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -75,16 +76,19 @@ int main(int argc, char **argv) {
   }
   printf("%ld %ld\n", n, bad);
   n = bad = 0;
+  static const float targets[5] = {6.0f, 5.5f, 5.0f, 4.5f, 4.0f};
   for (int it = 0; it < nts; ++it) {
+    volatile float T = targets[it % 5];
+    const float yT = one / T;
     const float ts = u2f(((uint32_t)(127 - 100 + rnd() % 201) << 23) | (rnd() & 0x7FFFFF));
     const float yts = one / ts;
     volatile float amax = ts * 2688.0f;
     for (int ia = 0; ia < 100000; ++ia) {
       const float ab = ldexpf(amax, (int)(rnd() % 53) - 40) * u2f(0x3f800000u | (rnd() & 0x7FFFFF)) * 0.75f;
       if (!(ab >= 0x1p-90f && ab <= 0x1p100f)) continue;
-      volatile float q = ab / six;
+      volatile float q = ab / T;
       volatile float s = q / ts;
-      const float sf = fminf(corrected_quotient(corrected_quotient(ab, 6.0f, y6), ts, yts), 448.0f);
+      const float sf = fminf(corrected_quotient(corrected_quotient(ab, T, yT), ts, yts), 448.0f);
       ++n;
       if (e4m3_byte(fminf(s, 448.0f)) != e4m3_byte(sf)) ++bad;
     }
