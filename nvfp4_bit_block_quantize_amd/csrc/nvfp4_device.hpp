@@ -141,11 +141,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 
 // ---- 16-point random Hadamard transform (in registers) -------------------------------------------
 // u <- (1/4) H16 D u: signs from the low 16 bits of sign_word, then the radix-2 butterfly with
-// strides 1, 2, 4, 8 (a + b to the lower, a - b to the upper slot), then the exact multiply by 1/4
-// (left to the caller when SCALE is false).
-// The butterfly and the 1/4 alone (H16 u / 4), for callers that applied the signs themselves.
-template <bool SCALE = true>
-__device__ __forceinline__ void rht16_butterfly(float (&u)[16]) {
+// strides 1, 2, 4, 8 (a + b to the lower, a - b to the upper slot), then the exact multiply by 1/4.
+__device__ __forceinline__ void rht16(float (&u)[16], uint32_t sign_word) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) u[t] = __uint_as_float(__float_as_uint(u[t]) ^ (((sign_word >> t) & 1u) << 31));
 #pragma unroll
   for (int h = 1; h < 16; h *= 2) {
 #pragma unroll
@@ -158,17 +157,8 @@ __device__ __forceinline__ void rht16_butterfly(float (&u)[16]) {
       }
     }
   }
-  if constexpr (SCALE) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) u[t] = u[t] * 0.25f;
-  }
-}
-
-template <bool SCALE = true>
-__device__ __forceinline__ void rht16(float (&u)[16], uint32_t sign_word) {
-#pragma unroll
-  for (int t = 0; t < 16; ++t) u[t] = __uint_as_float(__float_as_uint(u[t]) ^ (((sign_word >> t) & 1u) << 31));
-  rht16_butterfly<SCALE>(u);
+  for (int t = 0; t < 16; ++t) u[t] = u[t] * 0.25f;
 }
 
 // ---- fast division by a run-time invariant 32-bit divisor ----------------------------------------
