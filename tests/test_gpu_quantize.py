@@ -135,12 +135,13 @@ def _check_rht(oracle, x, flags, sign_seed, seed=0, stream_id=0, name=""):
     return float(diff.mean())
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("flags", [nv.NVFP4_COLWISE, nv.NVFP4_COLWISE | nv.NVFP4_SR, 0, nv.NVFP4_SR,
-                                   nv.NVFP4_COLWISE | nv.NVFP4_FOUR_OVER_SIX])
-def test_rht_quantize_matches_oracle(oracle, flags):
-    x = _gauss((528, 400), 7)
+                                   nv.NVFP4_COLWISE | nv.NVFP4_FOUR_OVER_SIX, nv.NVFP4_FOUR_OVER_SIX])
+def test_rht_quantize_matches_oracle(oracle, flags, dtype):
+    x = _gauss((528, 400), 7, dtype)
     synth.outlier_columns(x, 0.02, 20.0, seed=7, tensor_id=53)
-    frac = _check_rht(oracle, x, flags, sign_seed=7, seed=7, name=f"rht flags={flags}")
+    frac = _check_rht(oracle, x, flags, sign_seed=7, seed=7, name=f"rht flags={flags} {dtype}")
     assert frac == 0.0  # same butterfly order as the oracle: identical
 
 

@@ -40,9 +40,10 @@ def test_variant_matches_oracle(oracle, name, shape, flags, dtype):
     assert_quant_equal(q, ref, f"{name} {dtype}")
 
 
-@pytest.mark.parametrize("flags", [SRCH, F46 | TS4, SRCH | TS4])
-def test_variant_with_transform(oracle, flags):
-    x = synth.normal((128, 1024), 1.0, seed=9, tensor_id=81, dtype=torch.bfloat16)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("flags", [SRCH, F46 | TS4, SRCH | TS4, COL | SRCH])
+def test_variant_with_transform(oracle, flags, dtype):
+    x = synth.normal((128, 1024), 1.0, seed=9, tensor_id=81, dtype=dtype)
     q = nv.nvfp4_rht_quantize(x.cuda(), 7, flags=flags)
     torch.cuda.synchronize()
     ref = oracle.quantize(oracle_input(x), flags=flags, rht=True, sign_seed=7)
