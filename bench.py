@@ -282,23 +282,24 @@ def main():
     if w4a16:
         qb = nv.nvfp4_quantize(w, flags=fb, workspace=ws_b)
 
-    def q_a():
+    def q_a(src=None):
         if w4a16:
             return
+        src = x if src is None else src
         if rht:
-            nv.nvfp4_rht_quantize(x, 7, flags=fa, seed=7, out=qa, workspace=ws_a)
+            nv.nvfp4_rht_quantize(src, 7, flags=fa, seed=7, out=qa, workspace=ws_a)
         else:
-            nv.nvfp4_quantize(x, flags=fa, seed=7, out=qa, workspace=ws_a)
+            nv.nvfp4_quantize(src, flags=fa, seed=7, out=qa, workspace=ws_a)
 
-    def q_b():
+    def q_b(src=None):
         if w4a16:
             return
         if qw_fwd is not None:
-            nv.nvfp4_transpose(qw_fwd, out=qb)
+            nv.nvfp4_transpose(qw_fwd if src is None else src, out=qb)
         elif rht:
-            nv.nvfp4_rht_quantize(w, 7, flags=fb, out=qb, workspace=ws_b)
+            nv.nvfp4_rht_quantize(w if src is None else src, 7, flags=fb, out=qb, workspace=ws_b)
         else:
-            nv.nvfp4_quantize(w, flags=fb, out=qb, workspace=ws_b)
+            nv.nvfp4_quantize(w if src is None else src, flags=fb, out=qb, workspace=ws_b)
 
     def mm():
         if fused:
@@ -366,6 +367,36 @@ def main():
     qa_cold = cold_ms(q_a) if qbytes else 0.0
     qb_cold = cold_ms(q_b) if qbytes else 0.0
 
+    # The same calls streamed: back to back, each on its own copy of the input, with enough copies
+    # (512 MiB or more in all) that every call reads an input last touched more than the Infinity
+    # Cache's 256 MB ago, so each input comes from HBM.  A call timed alone after the flush above also
+    # carries the ~6 us between the flush kernel's end and the call's first kernel (event and
+    # dispatch; profiles/quantize_cold_fprop8b.md), which a call queued behind other work does not.
+    def stream_cold_ms(fn, src):
+        if torch.is_tensor(src):
+            nbytes = src.numel() * src.element_size()
+            copy = src.clone
+        else:  # a quantized tensor (the dgrad step's transpose input)
+            nbytes = src.data.numel() + src.scales.numel()
+            copy = lambda: nv.NVFP4Tensor(src.data.clone(), src.scales.clone(), src.tensor_scale.clone(),
+                                          src.rows, src.k, src.flags)
+        ncopy = 1 if nbytes >= (512 << 20) else -(-(512 << 20) // nbytes) + 1
+        copies = [copy() for _ in range(ncopy)]
+        reps = max(a.steps, 2 * ncopy)
+        for c in copies:
+            fn(c)
+        mm()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(copies[i % ncopy])
+        e1.record()
+        e1.synchronize()
+        del copies
+        return e0.elapsed_time(e1) / reps
+    qa_stream = stream_cold_ms(q_a, x) if qbytes else 0.0
+    qb_stream = stream_cold_ms(q_b, qw_fwd if qw_fwd is not None else w) if qbytes else 0.0
+
     # copy ceiling: a device-to-device copy of the bf16 X (read + write, the same buffer sizes as the
     # quantize inputs), back to back like the quantize calls
     copy_dst = torch.empty_like(x)
@@ -428,13 +459,19 @@ def main():
         "config": {"workload": workload, "M": M, "N": N, "K": K, "out": str(out_dtype).replace("torch.", "")},
         "components": {
             "quantize_warm_gbps": round(quant_gbps, 1),
-            "quantize_cold_gbps": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9, 1) if qbytes else None,
-            # (the cold rate: inputs flushed from the Infinity Cache, as a training step meets them)
-            "quantize_hbm_frac": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if qbytes else None,
+            # cold: every input read from HBM (calls back to back, each on an input copy last touched
+            # more than the Infinity Cache's size ago), as a training step meets them
+            "quantize_cold_gbps": round(qbytes / ((qa_stream + qb_stream) * 1e-3) / 1e9, 1) if qbytes else None,
+            "quantize_hbm_frac": round(qbytes / ((qa_stream + qb_stream) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if qbytes else None,
+            # each call alone after a 1 GiB flush read, between two events (includes the gap before
+            # the first kernel)
+            "quantize_cold_single_call_gbps": round(qbytes / ((qa_cold + qb_cold) * 1e-3) / 1e9, 1) if qbytes else None,
             "copy_ceiling_gbps": round(copy_gbps, 1),
             "quantize_frac_of_copy": round(quant_gbps / copy_gbps, 4) if qbytes else None,
-            "quantize_cold_a_ms": round(qa_cold, 4),
-            "quantize_cold_b_ms": round(qb_cold, 4),
+            "quantize_cold_a_ms": round(qa_stream, 4),
+            "quantize_cold_b_ms": round(qb_stream, 4),
+            "quantize_cold_single_call_a_ms": round(qa_cold, 4),
+            "quantize_cold_single_call_b_ms": round(qb_cold, 4),
             "quantize_a_ms": round(qa_ms, 4),
             "quantize_b_ms": round(qb_ms, 4),
             "quantize_algorithmic_bytes": qbytes,

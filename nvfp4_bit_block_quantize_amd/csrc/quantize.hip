@@ -631,7 +631,10 @@ __device__ __forceinline__ void absmax_chunk(const uint4 &v, u16x2 &m2, uint32_t
 
 template <int ESZ>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs p) {
-  constexpr int U = 8;  // loads in flight per lane
+  // Four 16-byte loads in flight per lane, and the remaining (< U) chunks of a lane issued together
+  // with clamped indices (a repeated chunk leaves a maximum unchanged): eight per lane, or a tail
+  // read one chunk at a time, measured 5-10% slower on inputs streamed from HBM.
+  constexpr int U = 4;
   p.x += blockIdx.y * p.g_x;
   p.partial += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   const uint32_t stride = gridDim.x * kAmaxThreads;
@@ -651,7 +654,13 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) absmax_chunk<ESZ>(v[u], m2, m4);
   }
-  for (; c < p.total_chunks; c += stride) absmax_chunk<ESZ>(*addr(c), m2, m4);
+  if (c < p.total_chunks) {
+    uint4 v[U - 1];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) v[u] = *addr(min(c + u * stride, p.total_chunks - 1));
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) absmax_chunk<ESZ>(v[u], m2, m4);
+  }
   const uint32_t m = ESZ == 2 ? (static_cast<uint32_t>(max(m2.x, m2.y)) << 16) : m4;
   write_partial<kAmaxThreads>(m, p.partial);
 }
