@@ -2,8 +2,10 @@
 
 This module holds no part of the quantization method: it only draws the input tensors (shapes,
 value distributions, outlier structure and MoE routing) that both the HIP library and the CPU
-oracle are fed with.  It uses PyTorch's CPU generator only (deterministic for a given seed and
-shape, independent of any GPU).
+oracle are fed with.  Every random number comes from its own C generator (synth/gen.c, built into
+synth/libsynth.so): Philox4x32-10 keyed by (seed, tensor id), Box-Muller in double, Fisher-Yates
+permutations.  No torch or numpy random generator is used, so the inputs depend only on the seed,
+the tensor id and the element index (and the C library's log, sin, cos and sqrt).
 
 Workloads (shapes stand in for the Llama-3-8B / Llama-3.1-405B FFN and the MoE expert layers that
 the pages' throughput and checkpoint results are quoted on; no dataset or trained weight is used):
@@ -16,22 +18,68 @@ the pages' throughput and checkpoint results are quoted on; no dataset or traine
 """
 from __future__ import annotations
 
+import ctypes
+import os
+
 import numpy as np
 import torch
 
+from . import build as _build
 
-def _gen(seed: int, tensor_id: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
-    g.manual_seed((int(seed) * 1_000_003 + int(tensor_id) * 7919 + 12345) & 0x7FFF_FFFF_FFFF_FFFF)
-    return g
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = os.path.join(_HERE, "libsynth.so")
+        src = os.path.join(_HERE, "gen.c")
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+            _build.build()
+        L = ctypes.CDLL(path)
+        P, i64, u64, u32, i32, dbl = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
+                                      ctypes.c_int, ctypes.c_double)
+        L.sg_normal.argtypes = [P, i64, u64, u32, dbl, i32, i32]
+        L.sg_normal.restype = None
+        L.sg_student_t.argtypes = [P, i64, i32, dbl, u64, u32, i32, i32]
+        L.sg_student_t.restype = None
+        L.sg_permutation.argtypes = [P, i64, u64, u32, u32]
+        L.sg_permutation.restype = None
+        L.sg_words.argtypes = [P, i64, u64, u32, u32]
+        L.sg_words.restype = None
+        _LIB = L
+    return _LIB
+
+
+def _empty(shape, dtype) -> torch.Tensor:
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"synthetic inputs are float32 or bfloat16, not {dtype}")
+    return torch.empty(shape, dtype=dtype)
+
+
+def permutation(n: int, seed=0, tensor_id=0, stream=0) -> np.ndarray:
+    """A seeded uniformly drawn permutation of range(n) (int64)."""
+    out = np.empty(n, dtype=np.int64)
+    _lib().sg_permutation(out.ctypes.data, n, int(seed) & (2**64 - 1), int(tensor_id) & 0xFFFFFFFF, stream)
+    return out
+
+
+def philox_words(ncalls: int, seed=0, tensor_id=0, stream=0) -> np.ndarray:
+    """The generator's raw Philox4x32-10 output words (4 per call), for its own tests."""
+    out = np.empty(4 * ncalls, dtype=np.uint32)
+    _lib().sg_words(out.ctypes.data, ncalls, int(seed) & (2**64 - 1), int(tensor_id) & 0xFFFFFFFF, stream)
+    return out
 
 
 def normal(shape, std=1.0, seed=0, tensor_id=0, dtype=torch.bfloat16) -> torch.Tensor:
-    """i.i.d. N(0, std^2) in fp32, rounded (RNE) to `dtype`."""
-    x = torch.randn(shape, generator=_gen(seed, tensor_id), dtype=torch.float32)
-    if std != 1.0:
-        x.mul_(std)
-    return x.to(dtype)
+    """i.i.d. N(0, std^2): element i is Box-Muller normal i of the (seed, tensor_id) stream times std,
+    rounded to fp32 and then (RNE) to `dtype`."""
+    out = _empty(shape, dtype)
+    _lib().sg_normal(out.data_ptr(), out.numel(), int(seed) & (2**64 - 1), int(tensor_id) & 0xFFFFFFFF,
+                     float(std), 1 if dtype == torch.bfloat16 else 0, _THREADS)
+    return out
 
 
 def outlier_columns(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_id=0) -> torch.Tensor:
@@ -40,7 +88,7 @@ def outlier_columns(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_
     n = int(round(frac * ncol))
     if n == 0:
         return x
-    cols = torch.randperm(ncol, generator=_gen(seed, tensor_id + 100))[:n]
+    cols = torch.from_numpy(permutation(ncol, seed, tensor_id + 100)[:n])
     x[:, cols] = (x[:, cols].float() * factor).to(x.dtype)
     return x
 
@@ -48,22 +96,19 @@ def outlier_columns(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_
 def outlier_entries(x: torch.Tensor, frac: float, factor: float, seed=0, tensor_id=0) -> torch.Tensor:
     """Scale round(frac * numel) seeded entries of x by `factor` (in place)."""
     n = int(round(frac * x.numel()))
-    idx = torch.randperm(x.numel(), generator=_gen(seed, tensor_id + 200))[:n]
+    idx = torch.from_numpy(permutation(x.numel(), seed, tensor_id + 200)[:n])
     flat = x.view(-1)
     flat[idx] = (flat[idx].float() * factor).to(x.dtype)
     return x
 
 
 def student_t(shape, nu=4, scale=1.0, seed=0, tensor_id=0, dtype=torch.bfloat16) -> torch.Tensor:
-    """scale * t_nu with t = z0 / sqrt(sum_{i=1..nu} z_i^2 / nu), z ~ N(0,1); computed in fp64."""
-    g = _gen(seed, tensor_id)
-    z0 = torch.randn(shape, generator=g, dtype=torch.float64)
-    chi = torch.zeros(shape, dtype=torch.float64)
-    for _ in range(nu):
-        z = torch.randn(shape, generator=g, dtype=torch.float64)
-        chi.add_(z * z)
-    t = z0 / torch.sqrt(chi / nu)
-    return (t * scale).to(dtype)
+    """scale * t_nu with t = z0 / sqrt(sum_{s=1..nu} z_s^2 / nu), z_s the element's normal of stream s;
+    computed in double, rounded to fp32, then (RNE) to `dtype`."""
+    out = _empty(shape, dtype)
+    _lib().sg_student_t(out.data_ptr(), out.numel(), int(nu), float(scale), int(seed) & (2**64 - 1),
+                        int(tensor_id) & 0xFFFFFFFF, 1 if dtype == torch.bfloat16 else 0, _THREADS)
+    return out
 
 
 def zipf_loads(n_experts=64, total=32768, s=1.1, seed=0) -> np.ndarray:
@@ -77,7 +122,7 @@ def zipf_loads(n_experts=64, total=32768, s=1.1, seed=0) -> np.ndarray:
     rem = total - int(m.sum())
     order = np.argsort(-(raw - m), kind="stable")
     m[order[:rem]] += 1
-    perm = torch.randperm(n_experts, generator=_gen(seed, 900)).numpy()
+    perm = permutation(n_experts, seed, 900)
     loads = np.zeros(n_experts, dtype=np.int64)
     loads[perm] = m  # rank r -> expert perm[r]
     return loads
@@ -96,7 +141,7 @@ def moe_routing(n_tokens=16384, n_experts=64, topk=2, s=1.1, seed=0):
     base = np.arange(n_tokens, dtype=np.int64)
     for k in range(topk):
         slot_token[k * n_tokens:(k + 1) * n_tokens] = base
-    relabel = torch.randperm(n_tokens, generator=_gen(seed, 901)).numpy()
+    relabel = permutation(n_tokens, seed, 901)
     slot_token = relabel[slot_token]
     return loads, slot_token
 
