@@ -41,6 +41,27 @@ def _ladder(v):
             + (v >= 3.5) + (v > 5.0)).astype(np.uint8)
 
 
+def test_e2m1_rne_exhaustive(oracle):
+    # every non-negative fp32 value, +0 up to +inf (2^31 - 2^23 + 1 bit patterns), in chunks on
+    # threads (numpy and the oracle's array call release the GIL)
+    from concurrent.futures import ThreadPoolExecutor
+    top = int(np.array([np.inf], dtype=np.float32).view(np.uint32)[0])
+    chunk = 1 << 24
+
+    def check(b0):
+        bits = np.arange(b0, min(b0 + chunk, top + 1), dtype=np.uint32)
+        v = bits.view(np.float32)
+        ref = ((v > 0.25).astype(np.uint8) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) + (v > 2.5)
+               + (v >= 3.5) + (v > 5.0)).astype(np.uint8)
+        got = oracle.e2m1_rne_index(v)
+        bad = np.flatnonzero(got != ref)
+        return (b0, int(bits[bad[0]]), int(got[bad[0]]), int(ref[bad[0]])) if bad.size else None
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        fails = [f for f in ex.map(check, range(0, top + 1, chunk)) if f is not None]
+    assert not fails, f"first mismatches (chunk, bits, oracle, ladder): {fails[:4]}"
+
+
 def test_e2m1_rne_matches_threshold_ladder(oracle):
     # a strided sweep over every fp32 bit pattern in [0, 8) plus +-64 ulps around each midpoint
     # and grid point
@@ -81,8 +102,9 @@ def _torch_e4m3_rne(s):
 def test_e4m3_rne_matches_torch_cast(oracle):
     vals = np.array([oracle.e4m3_value(b) for b in range(0x7F)], dtype=np.float64)
     mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    # every fp32 value within 4096 ulps of each midpoint and each E4M3 value, plus a strided sweep
     near = (np.concatenate([mids, vals.astype(np.float32)]).view(np.uint32)[:, None].astype(np.int64)
-            + np.arange(-8, 9)[None, :]).ravel()
+            + np.arange(-4096, 4097)[None, :]).ravel()
     top = np.array([448.0], dtype=np.float32).view(np.uint32)[0]
     bits = np.arange(0, top + 1, 997, dtype=np.int64)
     allb = np.concatenate([bits, near])
