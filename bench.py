@@ -762,7 +762,12 @@ def run_moe(a, nv, torch, synth, dev):
     gemm_tflops = flops / (mm_ms * 1e-3) / 1e12
     qa_bytes = quant_bytes(M, K, False)
     qb_bytes = E * quant_bytes(N, K, False)
-    tiles = int(sum((int(m) + 255) // 256 for m in loads)) * (N // 256)
+    # tiles of the grouped call: 256 x 256, except a group's last band when it holds at most 128 rows
+    # (a 128 x 256 tile of half the work, in a launch of its own)
+    half_bands = int(sum(1 for m in loads if 0 < int(m) % 256 <= 128))
+    full_bands = int(sum((int(m) + 255) // 256 for m in loads)) - half_bands
+    tiles = (full_bands + half_bands) * (N // 256)
+    padded_rows = 256 * full_bands + 128 * half_bands
     result = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -791,7 +796,8 @@ def run_moe(a, nv, torch, synth, dev):
             "gemm_ms": round(mm_ms, 4),
             "gemm_tflops": round(gemm_tflops, 1),
             "gemm_tiles": tiles,
-            "gemm_tile_fill": round(M * N / (tiles * 256 * 256), 4),
+            "gemm_half_tiles": half_bands * (N // 256),
+            "gemm_tile_fill": round(M / padded_rows, 4),
             "step_timing": "HIP graph replay of quantize(X_sorted) + grouped quantize(64 W_e) + grouped GEMM; "
                            "components: mean of back-to-back launches",
         },

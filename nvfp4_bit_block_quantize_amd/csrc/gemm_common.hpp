@@ -93,7 +93,14 @@ __device__ __forceinline__ void epilogue_scales(float ts_a, float ts_b, float &s
 // row segments per instruction; 16-byte chunk c of staged row r sits at c ^ (r mod chunks per row);
 // rows at or beyond row_end are not written.  Tiles cut by N, or C without 16-byte aligned rows,
 // take element stores.
-template <bool OUT_BF16, bool ONE>
+// HALF: a 128 x 256 tile (rows at or beyond m0 + 128 are never stored) whose four waves each hold
+// 128 rows x 64 columns: acc[j][i] for j < 2, wave w at columns 64 w.
+template <bool HALF>
+__device__ __forceinline__ uint32_t wave_row0(uint32_t wave) { return HALF ? 0u : (wave >> 1) * 128u; }
+template <bool HALF>
+__device__ __forceinline__ uint32_t wave_col0(uint32_t wave) { return HALF ? 64u * wave : (wave & 1) * 128u; }
+
+template <bool OUT_BF16, bool ONE, bool HALF>
 __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
                                              float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
@@ -101,11 +108,12 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
   // ONE: ts_a is the product of the two tensor scales (see epilogue_scales)
   auto sc = [&](float v) { return ONE ? v * ts_a : (v * ts_a) * ts_b; };
   constexpr int64_t ES = OUT_BF16 ? 2 : 4;
+  constexpr int JN = HALF ? 2 : 4;  // B fragments (32 columns each) per wave
   // (lane through an opaque copy: in a kernel that runs several tiles, the epilogue's per-lane
   // addresses are then formed here and not hoisted out of the tile loop into spilled registers)
   asm volatile("" : "+v"(lane));
   const uint32_t h = lane >> 5, l32 = lane & 31u;
-  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const uint32_t wm = wave_row0<HALF>(wave), wn = wave_col0<HALF>(wave);
   if (vec_store && n0 + BN <= N) {
     if (settle) {
       // all waves are done with the stages and the last (re-fetch) loads have landed
@@ -113,15 +121,16 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
       wait_lgkmcnt0();
       lds_barrier();
     }
-    constexpr uint32_t ROWB = 128 * ES, NCH = ROWB / 16;
+    constexpr uint32_t ROWB = 32 * JN * ES, NCH = ROWB / 16;
     uint8_t *const region = smem + wave * (32 * ROWB);
     uint8_t *const gbase = c + ((m0 + wm) * ldc + n0 + wn) * ES;
-    const int64_t rows_left = row_end - (m0 + wm);  // rows of the wave's quarter that exist
+    int64_t rows_left = row_end - (m0 + wm);  // rows of the wave's quarter that exist
+    if (HALF && rows_left > 128) rows_left = 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (32 * i >= rows_left) break;  // wave-uniform
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float v0 = sc(acc[j][i][4 * q]), v1 = sc(acc[j][i][4 * q + 1]);
@@ -131,11 +140,12 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
             const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
             const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
             const uint32_t ch = 4 * j + q;
-            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((ch ^ (l32 & 15)) * 16 + 8 * h)) =
+            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((ch ^ (l32 & (NCH - 1))) * 16 + 8 * h)) =
                 make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
           } else {
             const uint32_t ch = 8 * j + 2 * q + h;
-            *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & 31)) * 16) = make_float4(v0, v1, v2, v3);
+            *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & (NCH - 1))) * 16) =
+                make_float4(v0, v1, v2, v3);
           }
         }
       // the wave reads back its own rows (LDS accesses of one wave complete in order)
@@ -148,12 +158,13 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
     }
   } else {
     const int64_t row0 = m0 + wm + l32, col0 = n0 + wn + 4 * h;
+    const int64_t row_stop = HALF && row_end > m0 + 128 ? m0 + 128 : row_end;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = row0 + 32 * i;
-      if (row >= row_end) continue;
+      if (row >= row_stop) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t col = col0 + 32 * j + 8 * (r >> 2) + (r & 3);
@@ -170,7 +181,7 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
 
 // settle = false: smem is a region (waves x 32 x 128 B per element byte) that no wave reads and no
 // load in flight writes, so the staging neither waits for loads nor needs a barrier first.
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool HALF = false>
 __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
                                              float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
@@ -179,9 +190,9 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
   bool one;
   epilogue_scales(ts_a, ts_b, s1, s2, one);
   if (one)
-    store_c_rows<OUT_BF16, true>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
+    store_c_rows<OUT_BF16, true, HALF>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
   else
-    store_c_rows<OUT_BF16, false>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
+    store_c_rows<OUT_BF16, false, HALF>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
 }
 
 // Quantized epilogue: C = acc * ts_a * ts_b (the fp32 values store_c_tile would write) is quantized

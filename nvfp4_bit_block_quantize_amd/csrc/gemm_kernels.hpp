@@ -59,7 +59,8 @@ struct GemmKArgs {
   uint8_t *q_data, *q_scales;  // quantized output (NVFP4 out only)
   const float *q_ts;           // its tensor scale (input)
   float *amax;                 // nullable: max |C| is folded into *amax
-  int64_t row_begin[kMaxGroupsPerLaunch + 1];  // A rows of each group
+  int64_t row_begin[kMaxGroupsPerLaunch + 1];  // first A row of each group's tiles in this launch
+  int64_t row_end[kMaxGroupsPerLaunch];        // end of each group's A rows
   int32_t tile_begin[kMaxGroupsPerLaunch + 1]; // first tile of each group (prefix sums)
 };
 
@@ -188,7 +189,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   const int32_t tiles_m_g = (p.tile_begin[g + 1] - p.tile_begin[g]) / p.tiles_n;
   int32_t tm, tn;
   band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
-  const int64_t row_end = p.row_begin[g + 1];
+  const int64_t row_end = p.row_end[g];
   const uint8_t *b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
   const uint8_t *b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
   const float ts_a = *p.a_ts, ts_b = p.b_ts[p.group_base + g];
@@ -354,16 +355,16 @@ struct PipeLayout {
 // bank line, so a ds_read_b128 of a fragment is conflict-free.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3u; }
 
-// Scheduling pattern of one sub-step: 16 times one MFMA followed by up to V VALU instructions, and
-// L direct loads, one after each of MFMAs 0, 4, 8 ...: issuing a step's loads back to back stalls the
-// wave (the memory pipeline takes them one at a time) while no MFMA is queued.
-template <int V, int L = 0>
+// Scheduling pattern of one sub-step: NM times one MFMA followed by up to V VALU instructions, and
+// L direct loads, one after each of MFMAs 0, NM/4, NM/2 ...: issuing a step's loads back to back
+// stalls the wave (the memory pipeline takes them one at a time) while no MFMA is queued.
+template <int V, int L = 0, int NM = 16>
 __device__ __forceinline__ void mfma_valu_pattern() {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < NM; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-    if (q % 4 == 0 && q / 4 < L) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    if (q % (NM / 4) == 0 && q / (NM / 4) < L) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
   }
 }
 
@@ -385,9 +386,16 @@ __device__ __forceinline__ uint4 scale_pairs4(uint32_t w) {
   return r;
 }
 
-// OUT: 0 fp32 C, 1 bf16 C, 2 NVFP4 C (quantized in the epilogue)
-template <int OUT, bool A2D, bool B2D, bool PAIRED>
+// OUT: 0 fp32 C, 1 bf16 C, 2 NVFP4 C (quantized in the epilogue).
+// HALF: 128 x 256 tiles for the last rows of a group (at most 128 of them): each wave computes all
+// 128 rows against 64 of the 256 columns (its A fragments 0-3, B fragments 0-1), half the MFMAs
+// and three quarters of the decode of a full tile's wave.  The loads, the LDS ring and the waits
+// are those of the full tile (A rows 128-255 of the stage read clamped rows that no wave uses).
+template <int OUT, bool A2D, bool B2D, bool PAIRED, bool HALF>
 __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) void gemm_pipe_kernel(GemmKArgs p) {
+  static_assert(!HALF || OUT != 2, "the quantized epilogue takes full tiles only");
+  constexpr int JN = HALF ? 2 : 4;   // B fragments per wave
+  constexpr int NM = 4 * JN;         // MFMAs per sub-step
   using L = PipeLayout<PAIRED>;
   constexpr int kPStage = L::kStage, kLoadsPerStage = L::kLoadsPerStage;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::kBytes];
@@ -415,7 +423,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
     int32_t tm, tn;
     band_tile(local, p.tiles_n, tiles_m_g, tm, tn);
     t.g = g;
-    t.row_end = static_cast<int32_t>(p.row_begin[g + 1]);
+    t.row_end = static_cast<int32_t>(p.row_end[g]);
     t.b_data = p.b_data + static_cast<int64_t>(p.group_base + g) * p.b_group_data;
     t.b_scales = p.b_scales + static_cast<int64_t>(p.group_base + g) * p.b_group_scales;
     t.m0 = static_cast<int32_t>(p.row_begin[g]) + tm * BM;
@@ -427,7 +435,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t h = lane >> 5, l32 = lane & 31u;
-  const uint32_t wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const uint32_t wm = wave_row0<HALF>(wave), wn = wave_col0<HALF>(wave);
 
   // ---- direct-load sources: 32-bit per-lane offsets (an operand is below 2 GiB) from per-step bases
   const int64_t row_bytes = p.K / 2, KB = p.K / 16;
@@ -523,7 +531,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       ca[f] = *reinterpret_cast<const uint4 *>(st + kPA + rdA + 2048 * f + pos);
-      cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + rdB + 2048 * f + pos);
+      if (f < JN) cb[f] = *reinterpret_cast<const uint4 *>(st + kPB + rdB + 2048 * f + pos);
     }
   };
   // the scale words of step kt (blocks 4 h .. 4 h + 3): out of its pair's slot, or its stage
@@ -533,11 +541,11 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sa[f] = *reinterpret_cast<const uint32_t *>(src + rsA + par + kFrag * f);
-      sb[f] = *reinterpret_cast<const uint32_t *>(src + rsB + par + kFrag * f);
+      if (f < JN) sb[f] = *reinterpret_cast<const uint32_t *>(src + rsB + par + kFrag * f);
     }
   };
 
-  floatx16 acc[4][4];  // [B fragment j][A fragment i]
+  floatx16 acc[4][4];  // [B fragment j][A fragment i] (j < JN)
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -571,12 +579,12 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       psa[f] = scale_pairs4(rsa[f]);
-      psb[f] = scale_pairs4(rsb[f]);
+      if (f < JN) psb[f] = scale_pairs4(rsb[f]);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       afc[f] = decode8(ca0[f].x, psa[f].x);
-      bfc[f] = decode8(cb0[f].x, psb[f].x);
+      if (f < JN) bfc[f] = decode8(cb0[f].x, psb[f].x);
     }
   };
   start_tile(st0, slots);
@@ -622,28 +630,34 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const uint32_t da = mn < 4 ? pick(ca0[f], mn) : pick(ca1[f], mn - 4);
-          const uint32_t db = mn < 4 ? pick(cb0[f], mn) : pick(cb1[f], mn - 4);
           afn[f] = decode8(da, pick(psa[f], mn >> 1));
-          bfn[f] = decode8(db, pick(psb[f], mn >> 1));
+          if (f < JN) {
+            const uint32_t db = mn < 4 ? pick(cb0[f], mn) : pick(cb1[f], mn - 4);
+            bfn[f] = decode8(db, pick(psb[f], mn >> 1));
+          }
         }
       }
       if (m == 5) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const uint32_t loa = __builtin_amdgcn_perm(nsa[f], nsa[f], 0x01010000u);  // b0 b0 b1 b1
-          const uint32_t lob = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x01010000u);
           psa[f].x = scale_pair_cvt<false>(loa);
           psa[f].y = scale_pair_cvt<true>(loa);
-          psb[f].x = scale_pair_cvt<false>(lob);
-          psb[f].y = scale_pair_cvt<true>(lob);
+          if (f < JN) {
+            const uint32_t lob = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x01010000u);
+            psb[f].x = scale_pair_cvt<false>(lob);
+            psb[f].y = scale_pair_cvt<true>(lob);
+          }
         }
       } else if (m == 6) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           hia[f] = __builtin_amdgcn_perm(nsa[f], nsa[f], 0x03030202u);  // b2 b2 b3 b3
-          hib[f] = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x03030202u);
           psa[f].z = scale_pair_cvt<false>(hia[f]);
-          psb[f].z = scale_pair_cvt<false>(hib[f]);
+          if (f < JN) {
+            hib[f] = __builtin_amdgcn_perm(nsb[f], nsb[f], 0x03030202u);
+            psb[f].z = scale_pair_cvt<false>(hib[f]);
+          }
         }
       } else if (m == 7) {
         // this step's chunk 0 is dead: ca0 / cb0 hold the next step's chunk 0 (read after the
@@ -651,9 +665,11 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           psa[f].w = scale_pair_cvt<true>(hia[f]);
-          psb[f].w = scale_pair_cvt<true>(hib[f]);
           afn[f] = decode8(ca0[f].x, psa[f].x);
-          bfn[f] = decode8(cb0[f].x, psb[f].x);
+          if (f < JN) {
+            psb[f].w = scale_pair_cvt<true>(hib[f]);
+            bfn[f] = decode8(cb0[f].x, psb[f].x);
+          }
         }
       }
       // the loads of step kt + 2 (into the stage of step kt - 1, free since the barrier of step
@@ -664,27 +680,29 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
           if (m == 0) issue_pair(sc_tgt, gsb, pc, kt & 1);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JN; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfc[j], afc[i], acc[j][i], 0, 0, 0);
       // one MFMA, then the VALU work of the sub-step spread evenly (four decode instructions, five or
-      // six where scale conversions join them): the matrix pipe is never left behind a long run of
-      // VALU work (a wave issues in order)
+      // six where scale conversions join them; HALF: six decode instructions per MFMA, eight or nine
+      // with the conversions): the matrix pipe is never left behind a long run of VALU work (a wave
+      // issues in order)
+      constexpr int VD = HALF ? 6 : 4;
       if (m == 5)
-        mfma_valu_pattern<6>();
+        mfma_valu_pattern<HALF ? 9 : 6, 0, NM>();
       else if (m >= 6)
-        mfma_valu_pattern<5>();
+        mfma_valu_pattern<HALF ? 8 : 5, 0, NM>();
       else if (m == 0)
-        mfma_valu_pattern<4, 3>();
+        mfma_valu_pattern<VD, 3, NM>();
       else if (m < 4)
-        mfma_valu_pattern<4, PAIRED ? 2 : 3>();
+        mfma_valu_pattern<VD, PAIRED ? 2 : 3, NM>();
       else
-        mfma_valu_pattern<4>();
+        mfma_valu_pattern<VD, 0, NM>();
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         afc[f] = afn[f];
-        bfc[f] = bfn[f];
+        if (f < JN) bfc[f] = bfn[f];
       }
       if (m == 4) {
         // every wave holds this step's codes in registers (chunk 1 since sub-step 3's decode), and
@@ -735,14 +753,14 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
         if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(p.amax), __float_as_uint(amax));
       }
     } else if (!has_next) {
-      store_c_tile<OUT == 1>(acc, smem, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
-                             p.vec_store != 0, wave, lane);
+      store_c_tile<OUT == 1, HALF>(acc, smem, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
+                                   p.vec_store != 0, wave, lane);
     } else {
       // staged in tgt, the stage of the tile's last step: read by no wave since that step's barrier
       // and the target of the next tile's first loads, so every wave's read-back completes before
       // the barrier after it; the next tile's loads in flight are not waited for
-      store_c_tile<OUT == 1>(acc, tgt, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
-                             p.vec_store != 0, wave, lane, false);
+      store_c_tile<OUT == 1, HALF>(acc, tgt, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
+                                   p.vec_store != 0, wave, lane, false);
       wait_lgkmcnt0();
       lds_barrier();
     }
@@ -768,13 +786,18 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
 // workgroups (p.total_tiles, or fewer for the pipelined kernel with bf16 C and at least four K
 // steps, whose workgroups then run several tiles each).
 template <int OUT, bool A2D, bool B2D>
-hipError_t launch_variant(const GemmKArgs &p, int32_t grid, bool full, bool paired, hipStream_t stream) {
-  if (paired)
-    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+hipError_t launch_variant(const GemmKArgs &p, int32_t grid, bool full, bool paired, bool half, hipStream_t stream) {
+  if (half) {
+    // 128 x 256 tiles: the paired pipelined kernel with fp32 or bf16 C only
+    if constexpr (OUT == 2) return hipErrorInvalidValue;
+    else if (!paired) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (paired)
+    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if constexpr (OUT == 2)
     return hipErrorInvalidValue;  // the quantized epilogue exists in the paired kernel only
   else if (full)
-    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_pipe_kernel<OUT, A2D, B2D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_kernel<OUT == 1, A2D, B2D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

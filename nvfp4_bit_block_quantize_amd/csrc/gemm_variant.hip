@@ -10,6 +10,6 @@
 namespace nvfp4 {
 namespace gemm {
 template hipError_t launch_variant<NVFP4_OUT, (NVFP4_A2D != 0), (NVFP4_B2D != 0)>(const GemmKArgs &, int32_t, bool,
-                                                                                  bool, hipStream_t);
+                                                                                  bool, bool, hipStream_t);
 }  // namespace gemm
 }  // namespace nvfp4

@@ -199,3 +199,37 @@ def test_gemm_grouped_beyond_one_launch(oracle):
     data, scales = oracle.quantize_given_ts(c32.cpu().numpy(), np.float32(ts))
     np.testing.assert_array_equal(out.scales.cpu().numpy(), scales)
     np.testing.assert_array_equal(out.data.cpu().numpy(), data)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_grouped_half_tiles(oracle, out_dtype):
+    """Grouped GEMM whose groups end in bands of 1..128 rows (computed as 128 x 256 tiles in a launch
+    of their own) next to groups ending in 129..256 rows (full tiles): remainders at the boundaries
+    (1, 127, 128, 129, 255, 256, 257, 384, 385, 512), and more half tiles than compute units, so that
+    with bf16 C each workgroup of the half launch runs several tiles.  Every output is checked."""
+    rng = np.random.default_rng(41)
+    edge = [1, 127, 128, 129, 255, 256, 257, 384, 385, 512, 0, 2]
+    sizes = np.concatenate([edge, rng.integers(1, 129, 120)])
+    G, N, K = len(sizes), 768, 512
+    M = int(sizes.sum())
+    offs = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    print(f"[gemm] {G} groups, {M} rows, half tiles {3 * int(np.sum((sizes % 256 > 0) & (sizes % 256 <= 128)))}, "
+          f"out={out_dtype}", flush=True)
+    a = synth.normal((M, K), 1.0, seed=41, tensor_id=600)
+    w = torch.stack([synth.normal((N, K), 0.02 * (1 + g % 5), seed=41, tensor_id=601 + g) for g in range(G)])
+    qa = nv.nvfp4_quantize(a.cuda())
+    qb = nv.nvfp4_quantize_grouped(w.cuda())
+    ha, hb = _host(qa), _host(qb)
+    ts_b = qb.tensor_scale.cpu().numpy()
+    c = nv.nvfp4_gemm(qa, qb, out_dtype=out_dtype, group_offsets=offs).float().cpu().numpy()
+    worst = 0.0
+    for g in range(G):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 == r0:
+            continue
+        sub_a = {"data": ha["data"][r0:r1], "scales": ha["scales"][r0:r1], "ts": ha["ts"], "flags": 0}
+        sub_b = {"data": hb["data"][g * N:(g + 1) * N], "scales": hb["scales"][g * N:(g + 1) * N],
+                 "ts": ts_b[g], "flags": 0}
+        cref, bnd = oracle.gemm_ref(sub_a, sub_b, r1 - r0, N, K)
+        worst = max(worst, gemm_check(c[r0:r1], cref, bnd, out_dtype == torch.bfloat16, f"group {g} ({r1 - r0} rows)"))
+    print(f"max |err| / bound = {worst:.3e}")
