@@ -294,7 +294,7 @@ __device__ __forceinline__ float sse_pair(uint32_t w, float y0, float y1, float 
 template <int MODE>
 __device__ __forceinline__ void block_words(const float (&y)[16], float e, uint64_t i0, uint32_t key0, uint32_t key1,
                                             uint32_t stream_id, uint32_t &w0, uint32_t &w1) {
-  if (__builtin_isinf(e)) {
+  auto degenerate = [&]() {
     w0 = 0u;
     w1 = 0u;
 #pragma unroll
@@ -302,17 +302,29 @@ __device__ __forceinline__ void block_words(const float (&y)[16], float e, uint6
       w0 |= code_degenerate(y[t]) << (4 * t);
       w1 |= code_degenerate(y[8 + t]) << (4 * t);
     }
-  } else if constexpr (MODE == kSR) {
-    const uint64_t call = i0 >> 3;
-    const u32x4 r0 = philox4x32_10(static_cast<uint32_t>(call), static_cast<uint32_t>(call >> 32), stream_id, 0u,
-                                   key0, key1);
-    const u32x4 r1 = philox4x32_10(static_cast<uint32_t>(call + 1), static_cast<uint32_t>((call + 1) >> 32),
-                                   stream_id, 0u, key0, key1);
-    w0 = pack8_sr(y, e, r0);
-    w1 = pack8_sr(y + 8, e, r1);
+  };
+  if constexpr (MODE == kSR) {
+    if (__builtin_isinf(e)) {
+      degenerate();
+    } else {
+      const uint64_t call = i0 >> 3;
+      const u32x4 r0 = philox4x32_10(static_cast<uint32_t>(call), static_cast<uint32_t>(call >> 32), stream_id, 0u,
+                                     key0, key1);
+      const u32x4 r1 = philox4x32_10(static_cast<uint32_t>(call + 1), static_cast<uint32_t>((call + 1) >> 32),
+                                     stream_id, 0u, key0, key1);
+      w0 = pack8_sr(y, e, r0);
+      w1 = pack8_sr(y + 8, e, r1);
+    }
   } else {
+    // The conversion runs for every lane (an infinite factor gives undefined codes, replaced below);
+    // the rare infinite factor (S * ts underflowed) is patched under a wave-uniform branch, so that
+    // its per-element selects are not computed for every block (left to itself the compiler
+    // computed them unconditionally for the second candidate of the Four-over-Six encode).
     w0 = pack8_rne(y, e);
     w1 = pack8_rne(y + 8, e);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(__builtin_isinf(e)) != 0, 0)) {
+      if (__builtin_isinf(e)) degenerate();
+    }
   }
 }
 
