@@ -107,13 +107,13 @@ hipError_t launch_gemm(const GemmArgs &a) {
     ph.row_begin[ng] = p.row_begin[ng];
     ph.tile_begin[ng] = half_tiles;
     ph.total_tiles = half_tiles;
-    // The pipelined kernel with bf16 C and at least four K steps runs each workgroup over several
+    // The pipelined kernel with bf16 C (or fp32 C, paired) and at least four K steps runs each workgroup over several
     // tiles (one workgroup per compute unit, a multiple of 8 so that every workgroup keeps its XCD):
     // the next tile's first steps load under the last steps of the current one, and no workgroup
     // launch separates them.  Otherwise one workgroup per tile.
     auto grid_for = [&](int32_t n) {
       int32_t grid = n;
-      if (full && out == 1 && a.K / 128 >= 4) {
+      if (full && (out == 1 || (out == 0 && paired)) && a.K / 128 >= 4) {
         const int32_t cus = compute_units() / 8 * 8;
         if (cus >= 8 && cus < n) grid = cus;
       }

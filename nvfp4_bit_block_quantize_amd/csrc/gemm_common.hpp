@@ -100,7 +100,10 @@ __device__ __forceinline__ uint32_t wave_row0(uint32_t wave) { return HALF ? 0u 
 template <bool HALF>
 __device__ __forceinline__ uint32_t wave_col0(uint32_t wave) { return HALF ? 64u * wave : (wave & 1) * 128u; }
 
-template <bool OUT_BF16, bool ONE, bool HALF>
+// SPLIT (fp32 C of a full tile): the wave's 32-row pieces are staged one 64-column half at a time
+// (8 KB per wave instead of 16), so that the staging fits the 32 KB ring stage a multi-tile
+// workgroup hands the epilogue.
+template <bool OUT_BF16, bool ONE, bool HALF, bool SPLIT>
 __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
                                              float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
@@ -121,7 +124,9 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
       wait_lgkmcnt0();
       lds_barrier();
     }
-    constexpr uint32_t ROWB = 32 * JN * ES, NCH = ROWB / 16;
+    constexpr int JH = (SPLIT && !OUT_BF16 && !HALF) ? 2 : 1;  // column passes
+    constexpr int JP = JN / JH;                                  // B fragments per pass
+    constexpr uint32_t ROWB = 32 * JP * ES, NCH = ROWB / 16;
     uint8_t *const region = smem + wave * (32 * ROWB);
     uint8_t *const gbase = c + ((m0 + wm) * ldc + n0 + wn) * ES;
     int64_t rows_left = row_end - (m0 + wm);  // rows of the wave's quarter that exist
@@ -130,30 +135,36 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
     for (int i = 0; i < 4; ++i) {
       if (32 * i >= rows_left) break;  // wave-uniform
 #pragma unroll
-      for (int j = 0; j < JN; ++j)
+      for (int jh = 0; jh < JH; ++jh) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v0 = sc(acc[j][i][4 * q]), v1 = sc(acc[j][i][4 * q + 1]);
-          const float v2 = sc(acc[j][i][4 * q + 2]), v3 = sc(acc[j][i][4 * q + 3]);
-          if constexpr (OUT_BF16) {
-            // v_cvt_pk_bf16_f32: nearest-even, as bf16_rne
-            const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
-            const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
-            const uint32_t ch = 4 * j + q;
-            *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((ch ^ (l32 & (NCH - 1))) * 16 + 8 * h)) =
-                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-          } else {
-            const uint32_t ch = 8 * j + 2 * q + h;
-            *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & (NCH - 1))) * 16) =
-                make_float4(v0, v1, v2, v3);
+        for (int jj = 0; jj < JP; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = JP * jh + jj;
+            const float v0 = sc(acc[j][i][4 * q]), v1 = sc(acc[j][i][4 * q + 1]);
+            const float v2 = sc(acc[j][i][4 * q + 2]), v3 = sc(acc[j][i][4 * q + 3]);
+            if constexpr (OUT_BF16) {
+              // v_cvt_pk_bf16_f32: nearest-even, as bf16_rne
+              const bf16x2v lo = __builtin_convertvector((float2v){v0, v1}, bf16x2v);
+              const bf16x2v hi = __builtin_convertvector((float2v){v2, v3}, bf16x2v);
+              const uint32_t ch = 4 * jj + q;
+              *reinterpret_cast<uint2 *>(region + l32 * ROWB + ((ch ^ (l32 & (NCH - 1))) * 16 + 8 * h)) =
+                  make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+            } else {
+              const uint32_t ch = 8 * jj + 2 * q + h;
+              *reinterpret_cast<float4 *>(region + l32 * ROWB + (ch ^ (l32 & (NCH - 1))) * 16) =
+                  make_float4(v0, v1, v2, v3);
+            }
           }
-        }
-      // the wave reads back its own rows (LDS accesses of one wave complete in order)
+        // the wave reads back its own rows (LDS accesses of one wave complete in order, so the next
+        // pass's writes follow these reads)
 #pragma unroll
-      for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
-        const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
-        const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
-        if (32 * i + row < rows_left) *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * ldc * ES + u * 16) = v;
+        for (uint32_t t = 0; t < 32 * NCH / 64; ++t) {
+          const uint32_t row = t * (64 / NCH) + lane / NCH, u = lane % NCH;
+          const uint4 v = *reinterpret_cast<const uint4 *>(region + row * ROWB + ((u ^ (row & (NCH - 1))) * 16));
+          if (32 * i + row < rows_left)
+            *reinterpret_cast<uint4 *>(gbase + (32 * i + row) * ldc * ES + jh * ROWB + u * 16) = v;
+        }
       }
     }
   } else {
@@ -181,7 +192,7 @@ __device__ __forceinline__ void store_c_rows(floatx16 (&acc)[4][4], uint8_t *sme
 
 // settle = false: smem is a region (waves x 32 x 128 B per element byte) that no wave reads and no
 // load in flight writes, so the staging neither waits for loads nor needs a barrier first.
-template <bool OUT_BF16, bool HALF = false>
+template <bool OUT_BF16, bool HALF = false, bool SPLIT = false>
 __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *smem, uint8_t *c, int64_t ldc,
                                              int64_t m0, int64_t n0, int64_t row_end, int64_t N, float ts_a,
                                              float ts_b, bool vec_store, uint32_t wave, uint32_t lane,
@@ -190,9 +201,9 @@ __device__ __forceinline__ void store_c_tile(floatx16 (&acc)[4][4], uint8_t *sme
   bool one;
   epilogue_scales(ts_a, ts_b, s1, s2, one);
   if (one)
-    store_c_rows<OUT_BF16, true, HALF>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
+    store_c_rows<OUT_BF16, true, HALF, SPLIT>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
   else
-    store_c_rows<OUT_BF16, false, HALF>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
+    store_c_rows<OUT_BF16, false, HALF, SPLIT>(acc, smem, c, ldc, m0, n0, row_end, N, s1, s2, vec_store, wave, lane, settle);
 }
 
 // Quantized epilogue: C = acc * ts_a * ts_b (the fp32 values store_c_tile would write) is quantized

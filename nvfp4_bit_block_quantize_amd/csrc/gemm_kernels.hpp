@@ -722,8 +722,9 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
   uint8_t *cur = st0, *nxt = st1, *tgt = smem + 2 * kPStage;
   const float ts_a = *p.a_ts;
   for (int32_t s = 0;; ++s) {
-    // (bf16 C only, and with at least four K steps: the tile's C is staged in the one free stage,
-    // and the next tile's first scale pair is fetched from step KT - 4 on)
+    // (bf16 C, or fp32 C with paired scale loads (the unpaired fp32 kernel would spill), and at
+    // least four K steps: the tile's C is staged in the one free stage, fp32 one 64-column half at a
+    // time, and the next tile's first scale pair is fetched from step KT - 4 on)
     auto run_steps = [&](int32_t k0, int32_t k1, bool tail) __attribute__((always_inline)) {
       for (int32_t kt = k0; kt < k1; ++kt) {
         if constexpr (PAIRED) step(cur, nxt, tgt, slot_of((kt + 1) >> 1), slot_of((kt + 4) >> 1), kt, tail);
@@ -736,7 +737,7 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
     };
     const int32_t k_tail = KT > 4 ? KT - 4 : 0;
     run_steps(0, k_tail, false);
-    const int32_t next_tile = (OUT == 1 && KT >= 4) ? tile_at(s + 1) : -1;
+    const int32_t next_tile = (OUT == 1 || (OUT == 0 && PAIRED)) && KT >= 4 ? tile_at(s + 1) : -1;
     has_next = next_tile >= 0;
     if (has_next) nxt_t = describe(next_tile);
     run_steps(k_tail, KT, true);
@@ -759,8 +760,8 @@ __global__ __attribute__((visibility("hidden"))) __launch_bounds__(kThreads, 1) 
       // staged in tgt, the stage of the tile's last step: read by no wave since that step's barrier
       // and the target of the next tile's first loads, so every wave's read-back completes before
       // the barrier after it; the next tile's loads in flight are not waited for
-      store_c_tile<OUT == 1, HALF>(acc, tgt, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a, ts_b,
-                                   p.vec_store != 0, wave, lane, false);
+      store_c_tile<OUT == 1, HALF, true>(acc, tgt, p.c, p.ldc, cur_t.m0, cur_t.n0, cur_t.row_end, p.N, ts_a,
+                                         ts_b, p.vec_store != 0, wave, lane, false);
       wait_lgkmcnt0();
       lds_barrier();
     }
