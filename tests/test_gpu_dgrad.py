@@ -21,7 +21,7 @@ def _host(q):
             "ts": q.tensor_scale.cpu().numpy()[0], "flags": q.flags}
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 64), (1040, 272), (272, 1040)])
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 64), (1040, 272), (272, 1040), (160, 96), (4128, 288)])
 def test_transpose_equals_colwise_2d_quantization(oracle, shape):
     w = synth.normal(shape, 0.02, seed=3, tensor_id=70, dtype=torch.bfloat16)
     q = nv.nvfp4_quantize(w.cuda(), flags=B2)
