@@ -628,6 +628,9 @@ struct AmaxArgs {
   uint32_t flat;          // rows are contiguous (ldx == row length)
   uint32_t *partial;
   int64_t g_x;            // bytes between the inputs of consecutive groups (grid dimension y)
+  // 16-row bands for the 2D encode: a band is band_p slabs of 1024 chunks (band_p in 1, 2, 4, ..., 32,
+  // 256 workgroups), or 0
+  uint32_t band_p;
 };
 
 template <int ESZ>
@@ -658,7 +661,16 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs p) {
     return reinterpret_cast<const uint4 *>(p.x + static_cast<int64_t>(r) * p.ldx_bytes +
                                            static_cast<int64_t>(c - r * p.cpr.d) * 16);
   };
-  uint32_t c = blockIdx.x * kAmaxThreads + threadIdx.x;
+  // Workgroup w reads slab vw of each grid step (slab = 1024 chunks).  With 16-row bands of band_p
+  // slabs, vw relabels the workgroups so that the slabs of band b are read on XCD b mod 8 (workgroup
+  // w runs on XCD w mod 8): w = 8 g + x reads band 8 (g / band_p) + x of the step's bands, slab
+  // g mod band_p of it.  A bijection of the step's 256 slabs, so every chunk is read once.
+  uint32_t vw = blockIdx.x;
+  if (p.band_p != 0) {
+    const uint32_t g = blockIdx.x >> 3, x = blockIdx.x & 7u;
+    vw = p.band_p * (8u * (g / p.band_p) + x) + g % p.band_p;
+  }
+  uint32_t c = vw * kAmaxThreads + threadIdx.x;
   for (; c + (U - 1) * stride < p.total_chunks; c += U * stride) {
     uint4 v[U];
 #pragma unroll
@@ -694,15 +706,57 @@ struct RowArgs {
   float *rht_out;
   float ts_div;
   GroupStrides g;
+  // Pass 2 only: the pass-1 slab (blocks one pass-1 workgroup read per grid step; its XCD is the slab
+  // index mod 8), or 0 for the plain grid-stride order.
+  uint32_t slab;
 };
+
+// The blocks one lane of row1d_kernel encodes, in order: slab s_k = s0 + ds k (k < ns) of Z blocks,
+// piece h < H of 256 blocks (one per lane) within it.  Plain order: Z = 256, s0 = workgroup, ds =
+// grid.  XCD order (pass 2 after a pass 1 whose workgroups read slab s on XCD s mod 8): workgroup w
+// (on XCD w mod 8) walks the slabs of its own XCD from the top of the tensor down, so that it first
+// re-reads what that XCD's L2 still holds from the end of pass 1.
+struct BlockOrder {
+  int32_t s0, ds;
+  uint32_t nq, Z, lh;  // nq = ns * H, H = 1 << lh
+  __device__ __forceinline__ uint32_t block(uint32_t q) const {
+    return static_cast<uint32_t>(s0 + ds * static_cast<int32_t>(q >> lh)) * Z + (q & ((1u << lh) - 1u)) * 256u +
+           threadIdx.x;
+  }
+};
+
+__device__ __forceinline__ BlockOrder block_order(uint32_t n, uint32_t slab) {
+  static_assert(kThreads == 256, "one block per lane per 256-block piece");
+  BlockOrder o;
+  const uint32_t w = blockIdx.x, grid = gridDim.x;
+  if (slab == 0) {
+    const uint32_t S = (n + 255u) / 256u;
+    o.s0 = static_cast<int32_t>(w);
+    o.ds = static_cast<int32_t>(grid);
+    o.nq = w < S ? (S - 1u - w) / grid + 1u : 0u;
+    o.Z = 256u;
+    o.lh = 0;
+  } else {
+    const uint32_t x = w & 7u, k = w >> 3, g8 = grid >> 3;
+    const uint32_t S = (n + slab - 1u) / slab, J = x < S ? (S - x + 7u) / 8u : 0u;
+    const uint32_t lh = slab == 512u ? 1u : (slab == 1024u ? 2u : 0u);
+    o.s0 = static_cast<int32_t>(x + 8u * (J - 1u - k));
+    o.ds = -8 * static_cast<int32_t>(g8);
+    o.nq = k < J ? ((J - 1u - k) / g8 + 1u) << lh : 0u;
+    o.Z = slab;
+    o.lh = lh;
+  }
+  return o;
+}
 
 template <int ESZ, int MODE, bool RHT, bool PASS1>
 __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
   enter_group(p, p.nparts);
   p.partial_out += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   p.stream_id += blockIdx.y;
-  const uint32_t stride = gridDim.x * kThreads;
-  uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  const BlockOrder order = block_order(p.nblocks, PASS1 ? 0u : p.slab);
+  uint32_t q = 0;
+  uint32_t b = order.nq > 0 ? order.block(0) : p.nblocks;  // (>= nblocks: not a block to encode)
   auto src = [&](uint32_t blk) {
     const uint32_t r = fdiv(blk, p.kb);
     return p.x + static_cast<int64_t>(r) * p.ldx_bytes + static_cast<int64_t>(blk - r * p.kb.d) * 16 * ESZ;
@@ -724,9 +778,14 @@ __global__ __launch_bounds__(kThreads) void row1d_kernel(RowArgs p) {
     yts = 1.0f / ts;
   }
   uint32_t mx = 0;
-  while (b < p.nblocks) {
-    const uint32_t bn = b + stride;
+  for (; q < order.nq; ++q) {
+    const uint32_t bn = q + 1 < order.nq ? order.block(q + 1) : p.nblocks;
     if (bn < p.nblocks) nxt = load_raw16<ESZ>(src(bn));
+    if (b >= p.nblocks) {  // the top slab's missing blocks
+      cur = nxt;
+      b = bn;
+      continue;
+    }
     float y[16];
     if constexpr (RHT) {
       unpack16_signed<ESZ>(cur, y, p.sign_word);
@@ -795,6 +854,9 @@ struct Row2dArgs {
   float *ts_out;
   float ts_div;
   GroupStrides g;
+  // pass 1 left band b on XCD b mod 8 (AmaxArgs::band_p) and the grid is a multiple of 8: the waves
+  // take the bands of their own XCD, last-read bands first (the part still in that XCD's L2)
+  uint32_t affine;
 };
 
 // An empty asm that claims to modify the patch's registers: values unpacked from it before are not
@@ -895,19 +957,37 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   const int64_t KB = p.K / 16;
   uint32_t task = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  // XCD order: the XCD's tasks (band 8 j + x, segment) with band index j counted from the top;
+  // this wave takes XCD-local tasks v, v + 4 (grid / 8), ...
+  const uint32_t xcd = blockIdx.x & 7u, nbands = p.ntasks / p.nseg.d;
+  const uint32_t jx = xcd < nbands ? (nbands - xcd + 7u) / 8u : 0u;  // the XCD's bands
+  const uint32_t ntasks_x = jx * p.nseg.d;
+  if (p.affine) {
+    task = ((blockIdx.x >> 3) * kThreads + threadIdx.x) >> 6;
+  }
+  const uint32_t ntasks = p.affine ? ntasks_x : p.ntasks;
+  const uint32_t nwaves_x = p.affine ? (gridDim.x >> 3) * (kThreads / 64) : nwaves;
   Raw8<ESZ> v[16];
   auto start = [&](uint32_t tk, int64_t &r0, int64_t &c0) {
-    const uint32_t band = fdiv(tk, p.nseg);
+    uint32_t band, seg;
+    if (p.affine) {
+      const uint32_t j = fdiv(tk, p.nseg);
+      band = xcd + 8u * (jx - 1u - j);
+      seg = tk - j * p.nseg.d;
+    } else {
+      band = fdiv(tk, p.nseg);
+      seg = tk - band * p.nseg.d;
+    }
     r0 = static_cast<int64_t>(band) * 16;
-    c0 = static_cast<int64_t>(tk - band * p.nseg.d) * 512 + lane * 8;
+    c0 = static_cast<int64_t>(seg) * 512 + lane * 8;
   };
   int64_t r0 = 0, c0 = 0;
-  if (task < p.ntasks) {
+  if (task < ntasks) {
     start(task, r0, c0);
     load_patch<ESZ>(v, p.x + r0 * p.ldx_bytes + c0 * ESZ, p.ldx_bytes, c0 < p.K);
   }
   const float ts = tensor_scale(p.partial, p.nparts, p.ts_out, p.ts_div);
-  while (task < p.ntasks) {
+  while (task < ntasks) {
     const bool valid = c0 < p.K;  // K % 16 == 0: both lanes of a tile agree
     float ab = 0.0f;
 #pragma unroll
@@ -945,8 +1025,8 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
     }
     const int64_t wr0 = r0, wc0 = c0;
     // next task's loads go out before this task's stores
-    task += nwaves;
-    if (task < p.ntasks) {
+    task += nwaves_x;
+    if (task < ntasks) {
       start(task, r0, c0);
       load_patch<ESZ>(v, p.x + r0 * p.ldx_bytes + c0 * ESZ, p.ldx_bytes, c0 < p.K);
     }
@@ -1226,7 +1306,7 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   const int64_t ldx_bytes = a.ldx * ESZ;
   const uint32_t key0 = static_cast<uint32_t>(a.seed), key1 = static_cast<uint32_t>(a.seed >> 32);
   const uint8_t *x = static_cast<const uint8_t *>(a.x);
-  uint32_t nparts = 1;
+  uint32_t nparts = 1, band_p = 0;
   const uint32_t G = static_cast<uint32_t>(a.groups);
   const GroupStrides gs{a.x_group_bytes, a.R * a.K / 2, b2d ? (a.R / 16) * (a.K / 16) : a.R * (a.K / 16)};
 
@@ -1255,7 +1335,14 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint64_t total = static_cast<uint64_t>(a.rows) * cpr;
     nparts = clamp_grid((total + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads), kAmaxParts);
     AmaxArgs am{x, ldx_bytes, static_cast<uint32_t>(total), make_fastdiv(cpr > 0 ? cpr : 1),
-                static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace, a.x_group_bytes};
+                static_cast<uint32_t>(static_cast<int64_t>(row_bytes) == ldx_bytes), a.workspace, a.x_group_bytes, 0};
+    if (b2d && !colwise && row_bytes % 1024 == 0 && row_bytes > 0) {
+      // a 16-row band holds row_bytes 16-byte chunks, row_bytes / 1024 slabs; the relabelling is a
+      // bijection when each grid step holds a multiple of 8 whole bands
+      const uint64_t P = row_bytes / 1024;
+      if (P <= 32 && (P & (P - 1)) == 0 && nparts % (8 * P) == 0) am.band_p = static_cast<uint32_t>(P);
+    }
+    band_p = am.band_p;
     hipLaunchKernelGGL(amax_kernel<ESZ>, dim3(nparts, G), dim3(kAmaxThreads), 0, a.stream, am);
   } else if (!colwise) {
     nparts = clamp_grid((ra.nblocks + 4 * kThreads - 1) / (4 * kThreads), kPass1Parts);
@@ -1276,6 +1363,10 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   if (!colwise && !b2d) {
     ra.nparts = nparts;
     const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, kPass2Grid);
+    // pass 1 left each slab of 1024 16-byte chunks (amax_kernel) or of 256 blocks (the transform's
+    // row1d pass 1) on XCD (slab index mod 8) when its grid is a multiple of 8: pass 2 then takes the
+    // blocks in that XCD order, last-read slabs first (the part still in each XCD's L2)
+    ra.slab = (grid % 8 == 0 && nparts % 8 == 0) ? (a.rht ? 256u : 1024u / ESZ) : 0u;
     const dim3 g(grid, G), blk(kThreads);
 #define NVFP4_ROW(MODE_, RHT_) hipLaunchKernelGGL((row1d_kernel<ESZ, MODE_, RHT_, false>), g, blk, 0, a.stream, ra)
     if (a.rht) {
@@ -1301,8 +1392,9 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
   } else if (!colwise && b2d) {
     const uint32_t nseg = static_cast<uint32_t>((a.K + 511) / 512);
     Row2dArgs r2{x, ldx_bytes, static_cast<uint32_t>((a.R / 16) * nseg), make_fastdiv(nseg), a.K, a.workspace, nparts,
-                 a.data, a.scales, a.ts, ts_div, gs};
+                 a.data, a.scales, a.ts, ts_div, gs, 0};
     const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid);
+    r2.affine = (band_p != 0 && grid % 8 == 0) ? 1u : 0u;
     if (fos)
       hipLaunchKernelGGL((row2d_kernel<ESZ, true>), dim3(grid, G), dim3(kThreads), 0, a.stream, r2);
     else
