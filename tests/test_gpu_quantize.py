@@ -55,6 +55,19 @@ CASES = [
     ("col_sr", (528, 392), torch.bfloat16, nv.NVFP4_COLWISE | nv.NVFP4_SR),
     ("col_4over6", (528, 392), torch.bfloat16, nv.NVFP4_COLWISE | nv.NVFP4_FOUR_OVER_SIX),
     ("col_2d", (528, 400), torch.bfloat16, nv.NVFP4_COLWISE | nv.NVFP4_BLOCK2D),
+    # Shapes on which both passes take the XCD order (pass-1 grid and pass-2 grid multiples of 8;
+    # for 16x16 tiles, rows of 1024-byte multiples), with a band or slab count that is not a
+    # multiple of 8, so some XCDs own one band or slab fewer than others:
+    # 1D: 32670 blocks, pass-2 grid 128, 8 pass-1 parts, 63.8 slabs of 512 blocks
+    ("row_rne_xcd_order", (495, 1056), torch.bfloat16, 0),
+    ("row_sr_xcd_order", (495, 1056), torch.bfloat16, nv.NVFP4_SR),
+    ("row_4over6_xcd_order", (495, 1056), torch.bfloat16, nv.NVFP4_FOUR_OVER_SIX),
+    # 2D: 63 bands of one 1024-chunk slab each (8 pass-1 parts, pass-2 grid 16), bf16 and fp32
+    ("row_2d_xcd_order", (1008, 512), torch.bfloat16, nv.NVFP4_BLOCK2D),
+    ("row_2d_xcd_order_f32", (1008, 256), torch.float32, nv.NVFP4_BLOCK2D),
+    ("row_2d_4over6_xcd_order", (1008, 512), torch.bfloat16, nv.NVFP4_BLOCK2D | nv.NVFP4_FOUR_OVER_SIX),
+    # 2D: 260 bands of 8 slabs (256 pass-1 parts, pass-2 grid 520)
+    ("row_2d_xcd_order_wide", (4160, 4096), torch.bfloat16, nv.NVFP4_BLOCK2D),
 ]
 
 
@@ -143,6 +156,15 @@ def test_rht_quantize_matches_oracle(oracle, flags, dtype):
     synth.outlier_columns(x, 0.02, 20.0, seed=7, tensor_id=53)
     frac = _check_rht(oracle, x, flags, sign_seed=7, seed=7, name=f"rht flags={flags} {dtype}")
     assert frac == 0.0  # same butterfly order as the oracle: identical
+
+
+@pytest.mark.parametrize("flags", [0, nv.NVFP4_SR])
+def test_rht_row_xcd_order(oracle, flags):
+    # row-wise transform with both passes in XCD order: 32670 blocks, pass-1 grid 32, pass-2 grid 128,
+    # 127.6 slabs of 256 blocks
+    x = _gauss((495, 1056), 11)
+    frac = _check_rht(oracle, x, flags, sign_seed=3, seed=5, name=f"rht rows xcd order flags={flags}")
+    assert frac == 0.0
 
 
 def test_rht_sign_seed_changes_transform(oracle):
