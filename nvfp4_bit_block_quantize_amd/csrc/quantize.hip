@@ -714,8 +714,10 @@ struct RowArgs {
 // The blocks one lane of row1d_kernel encodes, in order: slab s_k = s0 + ds k (k < ns) of Z blocks,
 // piece h < H of 256 blocks (one per lane) within it.  Plain order: Z = 256, s0 = workgroup, ds =
 // grid.  XCD order (pass 2 after a pass 1 whose workgroups read slab s on XCD s mod 8): workgroup w
-// (on XCD w mod 8) walks the slabs of its own XCD from the top of the tensor down, so that it first
-// re-reads what that XCD's L2 still holds from the end of pass 1.
+// (on XCD w mod 8) walks the slabs of its own XCD, the last-read slab first.  Measured faster than
+// the plain order, the plain order reversed and the XCD order walked forwards, none of which differ
+// from one another; the L2 serves none of the re-reads (the same bytes are fetched from beyond it in
+// every order), so the gain is in how the reads meet the Infinity Cache and HBM.
 struct BlockOrder {
   int32_t s0, ds;
   uint32_t nq, Z, lh;  // nq = ns * H, H = 1 << lh
@@ -855,7 +857,7 @@ struct Row2dArgs {
   float ts_div;
   GroupStrides g;
   // pass 1 left band b on XCD b mod 8 (AmaxArgs::band_p) and the grid is a multiple of 8: the waves
-  // take the bands of their own XCD, last-read bands first (the part still in that XCD's L2)
+  // take the bands of their own XCD, last-read band first (the order of row1d_kernel's XCD order)
   uint32_t affine;
 };
 
@@ -1365,7 +1367,7 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint32_t grid = clamp_grid((ra.nblocks + kThreads - 1) / kThreads, kPass2Grid);
     // pass 1 left each slab of 1024 16-byte chunks (amax_kernel) or of 256 blocks (the transform's
     // row1d pass 1) on XCD (slab index mod 8) when its grid is a multiple of 8: pass 2 then takes the
-    // blocks in that XCD order, last-read slabs first (the part still in each XCD's L2)
+    // blocks in that XCD order, last-read slab first (measured faster; see BlockOrder)
     ra.slab = (grid % 8 == 0 && nparts % 8 == 0) ? (a.rht ? 256u : 1024u / ESZ) : 0u;
     const dim3 g(grid, G), blk(kThreads);
 #define NVFP4_ROW(MODE_, RHT_) hipLaunchKernelGGL((row1d_kernel<ESZ, MODE_, RHT_, false>), g, blk, 0, a.stream, ra)
