@@ -39,6 +39,10 @@ constexpr uint32_t kPass1Parts = 1024; // pass-1 workgroups at most (<= kMaxPart
 constexpr uint32_t kAmaxThreads = 1024; // amax_kernel workgroup: one per CU, 16 waves
 constexpr uint32_t kAmaxParts = 256;
 constexpr uint32_t kPass2Grid = 2048;  // persistent pass-2 workgroups (8 per CU)
+// row2d_kernel's cap: on W [14336x4096] 1024 workgroups (4 per CU) encode 2% faster than 2048 or
+// 4096 (0.0434-0.0436 against 0.0443-0.0447 ms per call from HBM), where row1d_kernel is fastest at
+// 2048 (X [8192x4096]: 0.0270 against 0.0280 ms at 1024)
+constexpr uint32_t kPass2Grid2D = 1024;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // ---- loads ----------------------------------------------------------------------------------------
@@ -1395,7 +1399,7 @@ hipError_t dispatch_quantize(const QuantArgs &a) {
     const uint32_t nseg = static_cast<uint32_t>((a.K + 511) / 512);
     Row2dArgs r2{x, ldx_bytes, static_cast<uint32_t>((a.R / 16) * nseg), make_fastdiv(nseg), a.K, a.workspace, nparts,
                  a.data, a.scales, a.ts, ts_div, gs, 0};
-    const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid);
+    const uint32_t grid = clamp_grid((r2.ntasks + 3) / 4, kPass2Grid2D);
     r2.affine = (band_p != 0 && grid % 8 == 0) ? 1u : 0u;
     if (fos)
       hipLaunchKernelGGL((row2d_kernel<ESZ, true>), dim3(grid, G), dim3(kThreads), 0, a.stream, r2);
