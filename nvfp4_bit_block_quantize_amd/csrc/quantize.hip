@@ -963,8 +963,9 @@ __global__ __launch_bounds__(kThreads) void row2d_kernel(Row2dArgs p) {
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   const int64_t KB = p.K / 16;
   uint32_t task = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  // XCD order: the XCD's tasks (band 8 j + x, segment) with band index j counted from the top;
-  // this wave takes XCD-local tasks v, v + 4 (grid / 8), ...
+  // XCD order: XCD x owns bands x, x + 8, ...; its task (j, segment) is a segment of the XCD's
+  // j-th band counted from the last (j = 0: the highest band x owns); this wave takes XCD-local
+  // tasks v, v + 4 (grid / 8), ...
   const uint32_t xcd = blockIdx.x & 7u, nbands = p.ntasks / p.nseg.d;
   const uint32_t jx = xcd < nbands ? (nbands - xcd + 7u) / 8u : 0u;  // the XCD's bands
   const uint32_t ntasks_x = jx * p.nseg.d;
