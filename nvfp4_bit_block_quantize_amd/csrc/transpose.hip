@@ -32,6 +32,12 @@ struct TransposeArgs {
   uint8_t *out_data, *out_scales;
   float *out_ts;
   int64_t R, K;  // input logical shape (R, K multiples of 16)
+  // Paired order (a one-dimensional grid): a tile reads 64 bytes of each of its 128 input rows, half
+  // of a 128-byte line, and the tile beside it reads the other half.  Workgroups L and L + 8 of
+  // each 16 run on the same XCD (workgroup i runs on XCD i mod 8) and start together, so they take
+  // the two tiles of a pair: each line is fetched into one L2 once instead of into two L2s.
+  // gx = tile columns (even); 0 for the plain two-dimensional grid.
+  uint32_t gx;
 };
 
 // 8 x 8 matrix of 4-bit codes, element (k, j) at bits 4j..4j+3 of d[k] -> element (k, j) at bits
@@ -56,7 +62,13 @@ template <bool W16>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t in_tile[kT * kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t out_tile[kT * kPitch];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kT, c0 = static_cast<int64_t>(blockIdx.x) * kT;
+  uint32_t bx = blockIdx.x, by = blockIdx.y;
+  if (p.gx != 0) {
+    const uint32_t L = blockIdx.x, pair = (L >> 4) * 8u + (L & 7u), hp = p.gx / 2u;
+    by = pair / hp;
+    bx = 2u * (pair - by * hp) + ((L >> 3) & 1u);
+  }
+  const int64_t r0 = static_cast<int64_t>(by) * kT, c0 = static_cast<int64_t>(bx) * kT;
   const uint32_t t = threadIdx.x;
   const int64_t in_row = p.K / 2, out_row = p.R / 2;
   // 1. load: piece i of thread t is input row (t + 256 i) / PR, codes CP ((t + 256 i) % PR) .. + CP
@@ -82,7 +94,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs p) {
     const int64_t br = r0 / 16 + (t >> 3), bc = c0 / 16 + (t & 7);
     if (br < p.R / 16 && bc < p.K / 16) p.out_scales[bc * (p.R / 16) + br] = p.in_scales[br * (p.K / 16) + bc];
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) *p.out_ts = *p.in_ts;
+  if (bx == 0 && by == 0 && t == 0) *p.out_ts = *p.in_ts;
   __syncthreads();
   // 2. transpose: lane -> block (br, bc), bc = lane % 16, br = 4 wave + lane / 16
   {
@@ -118,11 +130,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs p) {
 }  // namespace
 
 hipError_t launch_transpose(const TransposeLaunch &a) {
-  TransposeArgs p{a.in_data, a.in_scales, a.in_ts, a.out_data, a.out_scales, a.out_ts, a.R, a.K};
+  TransposeArgs p{a.in_data, a.in_scales, a.in_ts, a.out_data, a.out_scales, a.out_ts, a.R, a.K, 0};
   // at least one workgroup: it copies the tensor scale also when the tensor is empty
   const uint32_t gx = a.K > 0 ? static_cast<uint32_t>((a.K + kT - 1) / kT) : 1u;
   const uint32_t gy = a.R > 0 ? static_cast<uint32_t>((a.R + kT - 1) / kT) : 1u;
-  const dim3 grid(gx, gy);
+  // paired order when the tiles fill whole groups of 16 workgroups in pairs of columns
+  const uint64_t ntiles = static_cast<uint64_t>(gx) * gy;
+  const bool paired = gx % 2 == 0 && ntiles % 16 == 0 && ntiles < (uint64_t(1) << 31);
+  if (paired) p.gx = gx;
+  const dim3 grid = paired ? dim3(static_cast<uint32_t>(ntiles)) : dim3(gx, gy);
   if (a.R % 32 == 0 && a.K % 32 == 0) hipLaunchKernelGGL(transpose_kernel<true>, grid, dim3(256), 0, a.stream, p);
   else hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, a.stream, p);
   return hipGetLastError();

@@ -21,7 +21,10 @@ def _host(q):
             "ts": q.tensor_scale.cpu().numpy()[0], "flags": q.flags}
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 64), (1040, 272), (272, 1040), (160, 96), (4128, 288)])
+# (2000, 464) and (2048, 1024) run the paired tile order (an even number of 128-code tile columns,
+# a multiple of 16 tiles), the first with 8-byte pieces and ragged tiles on both axes
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 64), (1040, 272), (272, 1040), (160, 96), (4128, 288),
+                                   (2000, 464), (2048, 1024)])
 def test_transpose_equals_colwise_2d_quantization(oracle, shape):
     w = synth.normal(shape, 0.02, seed=3, tensor_id=70, dtype=torch.bfloat16)
     q = nv.nvfp4_quantize(w.cuda(), flags=B2)
